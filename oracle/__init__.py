@@ -1,0 +1,100 @@
+"""fp64 CPU oracle for the exact attention forward (ctypes wrapper over attn_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does, and this
+package imports nothing from the product.
+
+The oracle evaluates the plain definition of softmax attention in fp64 on inputs
+upcast exactly from their storage dtype: scores = scale * q.k (page
+"flash_attention_2.cu", forward kernel), top-left causal mask j <= i (same page,
+causal guard), softmax by max / exp / sum, O = P.V / l and L = m + ln(l) (same
+page, final normalisation). No tiling and no online recurrence.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile attn_oracle.c with gcc (no fast-math: IEEE fp64 throughout)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+           "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            f = lib.attn_oracle_fwd
+            f.restype = ctypes.c_int
+            dp = ctypes.POINTER(ctypes.c_double)
+            i64 = ctypes.c_int64
+            f.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                          ctypes.POINTER(ctypes.c_int64), i64, dp, dp, ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, threads: int | None = None):
+    """Exact attention forward in fp64.
+
+    q: [B,H,Nq,d], k and v: [B,H,Nk,d] (anything np.asarray turns into float64 exactly:
+    numpy arrays or CPU torch tensors already upcast with .double()).
+    rows: None for every row (returns O [B,H,Nq,d], L [B,H,Nq]) or an int64 array of flat
+    row ids (b*H + h)*Nq + i (returns O [len(rows), d], L [len(rows)]).
+    """
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float64))
+    k = np.ascontiguousarray(np.asarray(k, dtype=np.float64))
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float64))
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    if k.shape != (B, H, k.shape[2], d) or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    Nk = k.shape[2]
+    if rows is None:
+        nrows = B * H * Nq
+        o = np.empty((B, H, Nq, d), dtype=np.float64)
+        lse = np.empty((B, H, Nq), dtype=np.float64)
+        rows_p = None
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows.size
+        o = np.empty((nrows, d), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    lib = _load()
+    dp = ctypes.POINTER(ctypes.c_double)
+    rc = lib.attn_oracle_fwd(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
+                             B, H, Nq, Nk, d, float(scale), int(bool(causal)), rows_p, nrows,
+                             o.ctypes.data_as(dp), lse.ctypes.data_as(dp),
+                             int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"attn_oracle_fwd failed with status {rc}")
+    return o, lse
