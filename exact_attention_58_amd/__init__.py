@@ -1,0 +1,139 @@
+"""Python binding of the MI355X exact attention forward library (libfa_mi355x.so).
+
+Argument marshalling only: every step of the forward pass runs in the HIP kernels
+behind the C ABI declared in include/fa.h. PyTorch is used for device memory and
+streams. There is no fallback: if the library is missing, the calls raise.
+
+    fa_fwd(q, k, v, o, lse, scale, causal, stream=None)   # C-ABI fa_fwd on torch tensors
+    fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict
+    fa_status_str(code) -> str
+    attention(q, k, v, scale=None, causal=False) -> (o, lse)  # allocates o and lse
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
+EXPORTED = ("fa_fwd", "fa_status_str", "fa_select_config", "fa_version")
+DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, what: str = "fa_fwd"):
+        self.status = status
+        super().__init__(f"{what}: {fa_status_str(status)}")
+
+
+def is_built() -> bool:
+    return os.path.exists(LIB_PATH)
+
+
+def ensure_built() -> str:
+    """Builds the library only if no build is present (tests, smoke and bench use this)."""
+    if not is_built():
+        from . import build as _build
+        _build.build()
+    return LIB_PATH
+
+
+def lib():
+    """The loaded shared library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m exact_attention_58_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            i64, vp = ctypes.c_int64, ctypes.c_void_p
+            L.fa_fwd.restype = ctypes.c_int
+            L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                 ctypes.c_int, ctypes.c_int, vp]
+            L.fa_status_str.restype = ctypes.c_char_p
+            L.fa_status_str.argtypes = [ctypes.c_int]
+            ip = ctypes.POINTER(ctypes.c_int)
+            L.fa_select_config.restype = ctypes.c_int
+            L.fa_select_config.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int,
+                                           ctypes.c_int, ip, ip, ip, ip]
+            L.fa_version.restype = ctypes.c_int
+            L.fa_version.argtypes = []
+            _lib = L
+    return _lib
+
+
+def fa_status_str(code: int) -> str:
+    return lib().fa_status_str(int(code)).decode()
+
+
+def fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus: int = 256) -> dict:
+    dt = DTYPE_NAMES.get(dtype, dtype)
+    out = [ctypes.c_int(0) for _ in range(4)]
+    rc = lib().fa_select_config(int(dt), B, H, Nq, Nk, d, int(bool(causal)), int(num_cus),
+                                *[ctypes.byref(x) for x in out])
+    if rc != FA_OK:
+        raise FaError(rc, "fa_select_config")
+    return dict(zip(("Br", "Bc", "waves", "dpad"), (x.value for x in out)))
+
+
+def _torch_dtype_code(t):
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """Calls the C-ABI fa_fwd on contiguous [B,H,N,d] device tensors (o, lse preallocated).
+
+    stream: a torch.cuda.Stream, a raw hipStream_t int, or None for torch's current stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must be [B,H,Nq,d] and lse [B,H,Nq]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o must share one dtype; lse must be float32")
+    dev = q.device
+    if any(t.device != dev for t in (k, v, o, lse)):
+        raise ValueError("all tensors must be on one device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(dev):
+        rc = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
+                          handle)
+    if rc != FA_OK:
+        raise FaError(rc)
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocates o and lse (torch.empty) and runs fa_fwd; returns (o, lse)."""
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse

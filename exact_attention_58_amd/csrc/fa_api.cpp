@@ -1,0 +1,141 @@
+// fa_api.cpp -- C-ABI front end: argument checks, tile selection, launch.
+//
+// Argument checks run before any HIP call, so every error path can be exercised
+// without a GPU. The tile selector is a pure function of the sizes and the
+// compute-unit count: the analogue of choosing a tile size that fits the
+// on-chip memory and failing with an error when none does (page "Flash
+// Attention Shared Memory constraint", the group-size search).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kMaxDim = 128;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];  // 0 = not queried yet
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int dev_num_cus(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return 256;
+    int n = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    g_num_cus[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+    if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_EINVAL;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return FA_EINVAL;
+    int64_t bh, t;
+    if (!mul_ok(B, H, &bh)) return FA_EINVAL;
+    if (!mul_ok(bh, Nq, &t) || !mul_ok(t, d, &t)) return FA_EINVAL;
+    if (!mul_ok(bh, Nk, &t) || !mul_ok(t, d, &t)) return FA_EINVAL;
+    if (d > kMaxDim) return FA_EUNSUPPORTED;
+    // 32-bit index arithmetic inside one (batch, head): rows and row*d must fit.
+    if (Nq * d > INT32_MAX || Nk * d > INT32_MAX) return FA_EUNSUPPORTED;
+    if (B > INT32_MAX || H > INT32_MAX) return FA_EUNSUPPORTED;
+    return FA_OK;
+}
+
+}  // namespace
+
+int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                  int num_cus, TileConfig* out) {
+    (void)Nk;
+    (void)causal;
+    (void)num_cus;
+    TileConfig c{};
+    c.dpad = (int)((d + 31) / 32) * 32;
+    c.waves = 4;
+    c.br = 32 * c.waves;
+    if (dtype == FA_F32)
+        c.bc = c.dpad > 96 ? 32 : 64;
+    else
+        c.bc = 64;
+    // The grid must stay within the 32-bit launch limit.
+    const int64_t n_qtiles = (Nq + c.br - 1) / c.br;
+    if (n_qtiles * B * H > INT32_MAX) return FA_EUNSUPPORTED;
+    *out = c;
+    return FA_OK;
+}
+
+}  // namespace fa
+
+extern "C" {
+
+const char* fa_status_str(fa_status s) {
+    switch (s) {
+        case FA_OK: return "FA_OK: success";
+        case FA_EINVAL: return "FA_EINVAL: invalid argument";
+        case FA_EUNSUPPORTED: return "FA_EUNSUPPORTED: no kernel for this request";
+        case FA_ELAUNCH: return "FA_ELAUNCH: kernel launch failed";
+    }
+    return "unknown fa_status";
+}
+
+int fa_version(void) { return 1; }
+
+fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                           int causal, int num_cus, int* Br, int* Bc, int* waves, int* dpad) {
+    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    fa::TileConfig cfg;
+    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, num_cus > 0 ? num_cus : 256, &cfg);
+    if (rc != FA_OK) return (fa_status)rc;
+    if (Br) *Br = cfg.br;
+    if (Bc) *Bc = cfg.bc;
+    if (waves) *waves = cfg.waves;
+    if (dpad) *dpad = cfg.dpad;
+    return FA_OK;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                 int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                 fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
+    if (!std::isfinite(scale)) return FA_EINVAL;
+    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    const int esz = dtype == FA_F32 ? 4 : 2;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % esz != 0 ||
+        (uintptr_t)lse % 4 != 0)
+        return FA_EINVAL;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
+    fa::TileConfig cfg;
+    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, fa::dev_num_cus(dev), &cfg);
+    if (rc != FA_OK) return (fa_status)rc;
+
+    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
+                     (d * esz) % 16 == 0;
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = (int)B;
+    a.H = (int)H;
+    a.Nq = (int)Nq;
+    a.Nk = (int)Nk;
+    a.d = (int)d;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.causal = causal ? 1 : 0;
+    a.dtype = (int)dtype;
+    return fa::launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
+}  // extern "C"

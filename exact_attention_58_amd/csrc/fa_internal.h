@@ -1,0 +1,37 @@
+// fa_internal.h -- interface between the C-ABI front end (fa_api.cpp) and the
+// HIP kernels (fa_fwd_kernels.hip). Not installed, not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a forward kernel needs, already validated by the front end.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, Nq, Nk, d;
+    float scale_log2;  // softmax scale times log2(e): scores enter exp2 directly
+    int causal;
+    int dtype;         // fa_dtype value
+};
+
+// Tile configuration chosen by the selector.
+struct TileConfig {
+    int br;     // query rows per workgroup (32 per wave)
+    int bc;     // keys per K/V tile
+    int waves;  // waves per workgroup
+    int dpad;   // head dimension the kernel is compiled for (multiple of 32, >= d)
+};
+
+// Pure selection logic (no HIP calls). Returns 0 on success, 2 if no kernel fits.
+int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                  int causal, int num_cus, TileConfig* out);
+
+// Launches the kernel for `cfg` on `stream`; returns the hipError_t of the launch as int.
+int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream);
+
+}  // namespace fa

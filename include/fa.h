@@ -1,0 +1,111 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact attention forward library.
+ *
+ * One operation: exact scaled-dot-product attention forward with its per-row
+ * logsumexp,
+ *
+ *     O = softmax(scale * Q K^T + mask) V,      L_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * computed tile by tile with the online-softmax recurrence (running row max m,
+ * running row sum l, rescaled output accumulator), so the N x N score matrix
+ * never reaches device memory. Sources on the pages:
+ *   - page "flash_attention_2.cu" (leloykun/flash-hyperbolic-attention-minimal),
+ *     forward kernel and its host wrapper: the recurrence m, l, O; the final
+ *     O / l and L = m + log(l); the causal guard (key j visible to query i iff
+ *     j <= i); the wrapper returning {O, L} for [B, nh, N, d] inputs.
+ *   - page "Meta's xFormers has Attention kernel written in CUTLASS": parallel
+ *     work over queries as well as batch and heads in the forward pass; fp32
+ *     accumulation with a 16-bit output; residual handling for arbitrary
+ *     query and key lengths.
+ *   - page "Add Fused Multi-Head Attention example" (cuTile.jl PR #16): the
+ *     additive -Inf padding mask for keys beyond the key length, and exp2 with
+ *     the scale multiplied by 1/ln 2.
+ *   - page "Flash Attention Shared Memory constraint" (NNkernels.jl issue #10):
+ *     a tile configuration has to fit the on-chip memory, and the library
+ *     reports an error when none does.
+ *
+ * Everything here is plain C; the only HIP type is hipStream_t (passed as
+ * void* so that this header needs no HIP include).
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and o. lse is always fp32. */
+typedef enum {
+    FA_F32 = 0,  /* IEEE binary32; computed on fp32 MFMA, P kept in fp32      */
+    FA_F16 = 1,  /* IEEE binary16; fp16 MFMA operands, fp32 accumulation      */
+    FA_BF16 = 2  /* bfloat16; bf16 MFMA operands, fp32 accumulation           */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_EINVAL = 1,       /* bad argument: null pointer, size < 1, unknown dtype,
+                            non-finite scale, sizes whose products overflow    */
+    FA_EUNSUPPORTED = 2, /* valid request with no kernel for it (d > 128)      */
+    FA_ELAUNCH = 3       /* the HIP runtime reported an error at launch        */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward on the device, asynchronous on `stream`.
+ *
+ * Arguments
+ *   q      [B, H, Nq, d] device buffer, row-major, element type `dtype`
+ *   k, v   [B, H, Nk, d] device buffers, row-major, element type `dtype`
+ *   o      [B, H, Nq, d] device buffer written in full, element type `dtype`
+ *          (fp32 accumulator rounded to nearest even)
+ *   lse    [B, H, Nq] fp32 device buffer written in full: L = m + ln(l), the
+ *          natural-log logsumexp of the scaled, masked scores of each row
+ *   B, H, Nq, Nk, d   sizes, each >= 1; 1 <= d <= 128
+ *   scale  multiplies q . k before the mask and the softmax; any finite value
+ *          (0 and negative values included); 1/sqrt(d) is the usual choice
+ *   causal 0: every key is visible. non-zero: key j is visible to query i iff
+ *          j <= i (top-left alignment, also when Nq != Nk), so every row sees
+ *          key 0 and no row is empty
+ *   dtype  element type of q, k, v, o
+ *   stream hipStream_t to launch on (NULL = the null stream of the current
+ *          device). The current HIP device must own all five buffers.
+ *
+ * Ownership: the caller allocates every buffer; the library allocates
+ * nothing, keeps no per-call state and never synchronises. o must not alias
+ * q, k or v; lse must not alias anything. Buffers only need the alignment of
+ * their element type; 16-byte alignment (and d a multiple of 8 for 16-bit
+ * types, of 4 for fp32) enables the vectorised loads.
+ *
+ * Errors: arguments are checked before any HIP call. FA_EINVAL and
+ * FA_EUNSUPPORTED leave o and lse untouched. FA_ELAUNCH is returned when
+ * hipGetLastError() reports a failure after the launch.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 float scale, int causal, fa_dtype dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/*
+ * fa_select_config -- the tile configuration fa_fwd would launch for these
+ * sizes; pure host logic, no HIP call. Writes the query rows per workgroup
+ * (*Br), the keys per K/V tile (*Bc), the waves per workgroup (*waves) and
+ * the padded head dimension the kernel is compiled for (*dpad). Any output
+ * pointer may be NULL. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
+ * `num_cus` is the device's compute-unit count (256 on MI355X); it only
+ * affects the query-tile height when the grid would not fill the chip.
+ */
+fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                           int64_t d, int causal, int num_cus,
+                           int* Br, int* Bc, int* waves, int* dpad);
+
+/* Library version, for the Python binding's sanity check. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

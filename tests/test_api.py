@@ -1,0 +1,114 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the HIP runtime.
+
+No test here calls fa_fwd with arguments that pass validation (that would launch a kernel).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_58_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    fa.ensure_built()
+    return fa.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", src)))
+
+
+def test_header_symbols_are_exported(L):
+    names = header_functions()
+    assert set(names) == {"fa_fwd", "fa_status_str", "fa_select_config", "fa_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(fa.EXPORTED) == set(names)
+
+
+def test_version_and_status_strings(L):
+    assert L.fa_version() >= 1
+    for code, word in [(0, "FA_OK"), (1, "FA_EINVAL"), (2, "FA_EUNSUPPORTED"), (3, "FA_ELAUNCH")]:
+        assert fa.fa_status_str(code).startswith(word)
+    assert "unknown" in fa.fa_status_str(99)
+
+
+P = 4096  # a non-null, aligned fake pointer value: only ever passed with invalid arguments
+
+
+def call(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, Nq=8, Nk=8, d=64, scale=0.125, causal=0, dtype=2):
+    return L.fa_fwd(q, k, v, o, lse, B, H, Nq, Nk, d, ctypes.c_float(scale), causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(d=0), dict(B=-1), dict(Nk=-5),
+    dict(dtype=3), dict(dtype=-1),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=float("-inf")),
+    dict(B=2**40, H=2**40),                   # B*H overflows
+    dict(B=2**31, H=2**20, Nq=2**20, d=64),   # element count overflows int64
+    dict(q=P + 1, dtype=2),                   # misaligned for a 2-byte element
+    dict(o=P + 2, dtype=0),                   # misaligned for fp32
+    dict(lse=P + 2),                          # misaligned fp32 lse
+])
+def test_invalid_arguments(L, kw):
+    assert call(L, **kw) == fa.FA_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(d=129), dict(d=256), dict(Nq=2**26, d=64), dict(Nk=2**25, d=128)])
+def test_unsupported(L, kw):
+    assert call(L, **kw) == fa.FA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [1, 5, 32, 33, 64, 96, 100, 128])
+def test_select_config(dtype, d):
+    cfg = fa.fa_select_config(dtype, 4, 16, 4096, 4096, d, False)
+    assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
+    assert cfg["Br"] == 32 * cfg["waves"]
+    assert cfg["Bc"] in (32, 64)
+    # LDS of the chosen tiles (K with a 16-byte row pad, V padded for its read pattern)
+    s = 4 if dtype == "f32" else 2
+    vpad = 0 if dtype == "f32" else 32
+    lds = cfg["Bc"] * (cfg["dpad"] * s + 16) + cfg["Bc"] * (cfg["dpad"] * s + vpad)
+    assert lds * 2 <= 160 * 1024  # two workgroups per CU fit the 160 KiB LDS
+
+
+def test_select_config_errors():
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_select_config("bf16", 1, 1, 16, 16, 129, False)
+    assert e.value.status == fa.FA_EUNSUPPORTED
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_select_config("bf16", 0, 1, 16, 16, 64, False)
+    assert e.value.status == fa.FA_EINVAL
+
+
+def test_product_never_touches_oracle():
+    """The product package never imports the oracle, and the native sources never name it."""
+    pkg = os.path.join(ROOT, "exact_attention_58_amd")
+    imp = re.compile(r"^\s*(import\s+oracle|from\s+oracle|from\s+\.\.?\s*oracle)", re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            text = open(os.path.join(dirpath, f), errors="ignore").read() if f.endswith(
+                (".py", ".hip", ".cpp", ".h")) else ""
+            if f.endswith(".py"):
+                assert not imp.search(text), f
+                assert "attn_oracle" not in text and "importlib" not in text, f
+            elif text:
+                assert "oracle" not in text.lower(), f
+    assert "oracle" not in open(os.path.join(ROOT, "include", "fa.h")).read().lower()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(fa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        fa.lib()

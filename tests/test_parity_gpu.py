@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (max-abs, elementwise): O <= 1e-4 for fp32 and <= 2e-2 for fp16/bf16 inputs
+(unit-normal inputs, fp32 accumulation), L <= 1e-3. Large workloads run at their full size,
+in the launch configuration the benchmark times, and are compared on sampled rows the
+oracle computes one by one (first/last rows of tiles, ragged tails, random rows).
+"""
+import math
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_58_amd as fa
+import oracle
+from exact_attention_58_amd.workloads import DTYPES, WORKLOADS, make_inputs, make_random
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+TOL_L = 1e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.ensure_built()
+    fa.lib()
+
+
+def gpu_attention(q, k, v, scale, causal):
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    o, lse = fa.attention(qd, kd, vd, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def sample_rows(B, H, Nq, n_random=96, seed=0):
+    """Flat row ids: tile edges and tails of a few heads, plus random rows of all heads."""
+    rng = np.random.default_rng(seed)
+    bhs = sorted({0, (B * H) // 2, B * H - 1})
+    local = sorted({i for i in (0, 1, 31, 32, 63, 64, 127, 128, 255, 256, Nq // 2, Nq - 2, Nq - 1) if 0 <= i < Nq})
+    rows = [bh * Nq + i for bh in bhs for i in local]
+    rows += list(rng.integers(0, B * H * Nq, size=n_random))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def check(o_gpu, lse_gpu, o_ref, l_ref, dtype, what):
+    o_err = float(np.max(np.abs(o_gpu.double().numpy() - o_ref)))
+    l_err = float(np.max(np.abs(lse_gpu.double().numpy() - l_ref)))
+    say(f"  {what}: max|dO|={o_err:.3e} (tol {TOL_O[dtype]:.0e})  max|dL|={l_err:.3e} (tol {TOL_L:.0e})")
+    assert np.all(np.isfinite(o_gpu.double().numpy())) and np.all(np.isfinite(lse_gpu.numpy()))
+    assert o_err <= TOL_O[dtype], what
+    assert l_err <= TOL_L, what
+
+
+def full_check(q, k, v, scale, causal, dtype, what):
+    o, lse = gpu_attention(q, k, v, scale, causal)
+    o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), scale, causal)
+    check(o, lse, o_ref, l_ref, dtype, what)
+    return o, lse
+
+
+# ------------------------------------------------------------------ the named workloads
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload(name):
+    w = WORKLOADS[name]
+    say(f"workload {name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} {w.dtype} causal={w.causal}")
+    q, k, v = make_inputs(w)
+    o, lse = gpu_attention(q, k, v, w.softmax_scale, w.causal)
+    small = w.B * w.H * w.Nq * w.Nk * w.d <= 2 ** 35
+    if small:
+        o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), w.softmax_scale, w.causal)
+        check(o, lse, o_ref, l_ref, w.dtype, f"{name} all rows")
+    else:
+        rows = sample_rows(w.B, w.H, w.Nq, seed=w.seed)
+        o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), w.softmax_scale, w.causal,
+                                            rows=rows)
+        check(o.reshape(-1, w.d)[rows], lse.reshape(-1)[rows], o_ref, l_ref, w.dtype,
+              f"{name} {len(rows)} sampled rows")
+
+
+# ------------------------------------------------------------------ ragged / shape sweep
+
+SWEEP = []
+for dt in ("bf16", "f16", "f32"):
+    for d in (32, 64, 96, 128, 40, 5):
+        for (Nq, Nk) in ((1, 1), (17, 63), (64, 65), (129, 127), (200, 1000), (300, 300)):
+            for causal in (False, True):
+                SWEEP.append((dt, d, Nq, Nk, causal))
+
+
+@pytest.mark.parametrize("dt,d,Nq,Nk,causal", SWEEP)
+def test_shape_sweep(dt, d, Nq, Nk, causal):
+    seed = zlib.crc32(repr((dt, d, Nq, Nk, causal)).encode()) % 100000
+    B, H = 2, 3
+    q = make_random((B, H, Nq, d), dt, seed)
+    k = make_random((B, H, Nk, d), dt, seed + 1)
+    v = make_random((B, H, Nk, d), dt, seed + 2)
+    full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} d={d} Nq={Nq} Nk={Nk} causal={causal}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.9])
+def test_scale_values(dt, scale):
+    q = make_random((1, 2, 150, 64), dt, 11)
+    k = make_random((1, 2, 170, 64), dt, 12)
+    v = make_random((1, 2, 170, 64), dt, 13)
+    for causal in (False, True):
+        full_check(q, k, v, scale, causal, dt, f"{dt} scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_large_magnitude_scores(dt):
+    """Scores of order +-100: exercises the running max and the rescale path."""
+    q = make_random((1, 2, 257, 64), dt, 21, std=4.0)
+    k = make_random((1, 2, 700, 64), dt, 22, std=4.0)
+    v = make_random((1, 2, 700, 64), dt, 23)
+    for causal in (False, True):
+        full_check(q, k, v, 0.125, causal, dt, f"{dt} large scores causal={causal}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+def test_increasing_scores_force_rescales(dt):
+    """Scores that grow along the keys: every tile raises the row max by more than the
+    rescale threshold, so O and l are rescaled on every tile."""
+    Nk, d = 640, 64
+    q = torch.zeros((1, 1, 130, d), dtype=torch.float32)
+    q[..., 0] = 1.0
+    k = torch.zeros((1, 1, Nk, d), dtype=torch.float32)
+    k[..., 0] = torch.arange(Nk, dtype=torch.float32) * 0.25
+    v = make_random((1, 1, Nk, d), "f32", 31)
+    q, k, v = (t.to(DTYPES[dt]) for t in (q, k, v))
+    for causal in (False, True):
+        full_check(q, k, v, 1.0, causal, dt, f"{dt} growing scores causal={causal}")
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_invariants(dt, causal):
+    B, H, N, d = 1, 2, 300, 64
+    q = make_random((B, H, N, d), dt, 41)
+    k = make_random((B, H, N, d), dt, 42)
+    v = make_random((B, H, N, d), dt, 43)
+    tol = TOL_O[dt]
+    # V = ones -> O = ones
+    o, _ = gpu_attention(q, k, torch.ones_like(v), 0.125, causal)
+    assert float((o.double() - 1).abs().max()) <= tol
+    # identical keys -> O = mean of the visible V rows; L = scale*q.k + ln(count)
+    kk = k[:, :, :1].expand(B, H, N, d).contiguous()
+    o, lse = gpu_attention(q, kk, v, 0.125, causal)
+    vd = v.double()
+    if causal:
+        mean = torch.cumsum(vd, dim=2) / torch.arange(1, N + 1, dtype=torch.float64)[:, None]
+        cnt = torch.arange(1, N + 1, dtype=torch.float64)
+    else:
+        mean = vd.mean(dim=2, keepdim=True).expand_as(vd)
+        cnt = torch.full((N,), float(N), dtype=torch.float64)
+    assert float((o.double() - mean).abs().max()) <= tol
+    lref = 0.125 * (q.double() * kk.double()[:, :, :1]).sum(-1) + torch.log(cnt)
+    assert float((lse.double() - lref).abs().max()) <= TOL_L
+    # causal row 0 -> O[0] = V[0]
+    if causal:
+        o, lse = gpu_attention(q, k, v, 0.125, True)
+        assert float((o[:, :, 0].double() - v[:, :, 0].double()).abs().max()) <= tol
+    # duplicated K/V (non-causal): O unchanged, L + ln 2
+    if not causal:
+        o1, l1 = gpu_attention(q, k, v, 0.125, False)
+        o2, l2 = gpu_attention(q, torch.cat([k, k], 2), torch.cat([v, v], 2), 0.125, False)
+        assert float((o1.double() - o2.double()).abs().max()) <= tol
+        assert float((l2.double() - l1.double() - math.log(2)).abs().max()) <= TOL_L
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_deterministic(dt):
+    q = make_random((2, 4, 512, 128), dt, 51)
+    k = make_random((2, 4, 777, 128), dt, 52)
+    v = make_random((2, 4, 777, 128), dt, 53)
+    a = gpu_attention(q, k, v, 0.09, True)
+    b = gpu_attention(q, k, v, 0.09, True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [64, 40, 5])
+def test_canaries_and_unaligned_buffers(dt, d):
+    """Outputs carved out of larger buffers: the guard regions stay untouched. With a one-
+    element offset the pointers lose 16-byte alignment and the scalar-load kernel runs."""
+    torch_dt = DTYPES[dt]
+    B, H, Nq, Nk = 1, 3, 77, 99
+    q = make_random((B, H, Nq, d), dt, 61)
+    k = make_random((B, H, Nk, d), dt, 62)
+    v = make_random((B, H, Nk, d), dt, 63)
+    for off in (0, 1):
+        pad = 256
+        n_o = B * H * Nq * d
+        obuf = torch.full((n_o + 2 * pad,), 7.0, dtype=torch_dt, device="cuda")
+        lbuf = torch.full((B * H * Nq + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+
+        def carve(t):
+            buf = torch.empty(t.numel() + off, dtype=torch_dt, device="cuda")
+            view = buf[off:].view(t.shape)
+            view.copy_(t.cuda())
+            return view
+
+        qd, kd, vd = carve(q), carve(k), carve(v)
+        o = obuf[pad + off:pad + off + n_o].view(B, H, Nq, d)
+        lse = lbuf[pad:pad + B * H * Nq].view(B, H, Nq)
+        fa.fa_fwd(qd, kd, vd, o, lse, 0.3, True)
+        torch.cuda.synchronize()
+        assert torch.all(obuf[:pad + off] == 7.0) and torch.all(obuf[pad + off + n_o:] == 7.0)
+        assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[pad + B * H * Nq:] == 7.0)
+        o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), 0.3, True)
+        check(o.cpu(), lse.cpu(), o_ref, l_ref, dt, f"{dt} d={d} offset={off}")
+
+
+def test_causal_more_queries_than_keys():
+    q = make_random((1, 2, 300, 64), "bf16", 71)
+    k = make_random((1, 2, 100, 64), "bf16", 72)
+    v = make_random((1, 2, 100, 64), "bf16", 73)
+    full_check(q, k, v, 0.125, True, "bf16", "causal Nq > Nk (top-left)")
+
+
+def test_stream_argument():
+    """The kernel runs on the stream it is given."""
+    q = make_random((1, 2, 256, 64), "bf16", 81).cuda()
+    k = make_random((1, 2, 256, 64), "bf16", 82).cuda()
+    v = make_random((1, 2, 256, 64), "bf16", 83).cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = fa.attention(q, k, v, causal=True, stream=s)
+    s.synchronize()
+    o_ref, l_ref = oracle.attention_fwd(q.cpu().double(), k.cpu().double(), v.cpu().double(), 0.125, True)
+    check(o.cpu(), lse.cpu(), o_ref, l_ref, "bf16", "side stream")
