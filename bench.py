@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one fa_fwd call (the whole forward: Q load, K/V staging, QK^T, masks, online
+softmax, PV, epilogue) over one batch of synthetic inputs already resident in HBM.
+
+Headline workload: the pages' benchmark shape, B=4 H=4 Nq=Nk=4096 d=64 fp32 non-causal
+(page "Add Fused Multi-Head Attention example"). The same JSON line carries every other
+workload (the bf16 d=128 causal/non-causal pair, the long causal bf16 run and the ragged
+fp16 run), each with its TFLOP/s, fraction of the dtype's dense MFMA peak and kernel time,
+a short-sequence HBM sweep (GB/s) and the fp64 CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (no sparsity), TFLOP/s, and HBM3E bandwidth, GB/s.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_58_amd", "csrc", "fa_fwd_kernels.hip")
+
+# HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch, scaled by the factor a plain copy kernel of known size reads on the same
+# counters), keyed by workload, valid only for the kernel source whose sha256 prefix is
+# recorded. Filled in from the committed profiles; a source change makes it stale (null).
+TRAFFIC = {}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def time_workload(fa, torch, w, steps, warmup, inputs=None):
+    """Runs `steps` back-to-back fa_fwd calls on torch's current stream.
+
+    Returns (wall ms per step, average launch duration in ms from HIP events recorded on
+    the launch stream around the timed region)."""
+    from exact_attention_58_amd.workloads import make_inputs
+    dev = torch.device("cuda:0")
+    if inputs is None:
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+    else:
+        q, k, v = inputs
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fa.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    del o, lse
+    return wall_ms, ev_ms
+
+
+def roofline_for(w, ev_ms, sha):
+    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    tr = TRAFFIC.get(w.name)
+    traffic = tr["bytes"] if tr and tr.get("kernel_sha") == sha else None
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def hbm_sweep(fa, torch, steps):
+    """Short sequences (HBM-bound): bf16 d=128 non-causal, N in {128, 256, 512}, three
+    rotating input sets larger than the 256 MB Infinity Cache; GB/s = algorithmic bytes / t."""
+    from exact_attention_58_amd.workloads import Workload, make_random
+    dev = torch.device("cuda:0")
+    out = []
+    for N, B, H in ((128, 64, 128), (256, 32, 128), (512, 16, 128)):
+        w = Workload(f"short_N{N}", B, H, N, N, 128, "bf16", False, seed=100 + N)
+        sets = []
+        for s in range(3):
+            q = make_random((B, H, N, 128), "bf16", 1000 * N + 3 * s).to(dev)
+            k = make_random((B, H, N, 128), "bf16", 1000 * N + 3 * s + 1).to(dev)
+            v = make_random((B, H, N, 128), "bf16", 1000 * N + 3 * s + 2).to(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+            sets.append((q, k, v, o, lse))
+        stream = torch.cuda.current_stream(dev)
+        for i in range(3):
+            fa.fa_fwd(*sets[i], w.softmax_scale, False, stream)
+        torch.cuda.synchronize(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = max(3, steps)
+        e0.record(stream)
+        for i in range(n):
+            fa.fa_fwd(*sets[i % 3], w.softmax_scale, False, stream)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1) / n
+        gbs = w.io_bytes / (ms * 1e-3) / 1e9
+        out.append({"N": N, "B": B, "H": H, "d": 128, "ms": round(ms, 4), "GB_per_s": round(gbs, 1),
+                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "tflops": round(w.flops / (ms * 1e-3) / 1e12, 1)})
+        del sets
+    # attainable yardstick: a 2 GiB device-to-device copy
+    a = torch.empty(2 ** 30, dtype=torch.int16, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / 5
+    copy_gbs = 2 * a.numel() * 2 / (ms * 1e-3) / 1e9
+    del a, b
+    return out, round(copy_gbs, 1)
+
+
+def cpu_baseline(w, target_s: float = 15.0):
+    """The fp64 oracle as it stands, on the host cores, on a bounded row sample."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_58_amd.workloads import make_inputs
+    q, k, v = make_inputs(w)
+    qd, kd, vd = q.double(), k.double(), v.double()
+    threads = oracle.default_threads()
+    total_rows = w.B * w.H * w.Nq
+    per_row = 4.0 * w.Nk * w.d  # non-causal rows; the headline workload is non-causal
+
+    def run(nrows):
+        rows = np.linspace(0, total_rows - 1, nrows).round().astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attention_fwd(qd, kd, vd, w.softmax_scale, w.causal, rows=rows, threads=threads)
+        return time.perf_counter() - t0, len(rows)
+
+    dt, n = run(max(threads * 8, 256))
+    rate = n / dt
+    n2 = int(min(total_rows, max(n, rate * target_s)))
+    dt, n = run(n2)
+    flops = n * per_row
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {total_rows} query rows of {w.name} (evenly spaced over all heads), "
+                      f"{dt:.1f} s wall, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pages_f32")
+    ap.add_argument("--quick", action="store_true", help="headline only: no other workloads, sweep or CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the forward is measured on a single MI355X "
+              "(multi-GPU sharding is not built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_58_amd as fa
+    from exact_attention_58_amd.workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fa.ensure_built()
+    fa.lib()
+    sha = kernel_sha()
+    props = torch.cuda.get_device_properties(0)
+
+    w = WORKLOADS[args.workload]
+    log(f"headline {w.name}: {args.warmup} warmup + {args.steps} timed steps")
+    torch.cuda.synchronize()
+    wall_ms, ev_ms = time_workload(fa, torch, w, args.steps, args.warmup)
+    tflops = w.flops / (wall_ms * 1e-3) / 1e12
+    log(f"  {w.name}: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/launch (events), {tflops:.1f} TFLOP/s")
+
+    also = []
+    sweep, copy_gbs = None, None
+    if not args.quick:
+        for name, ow in WORKLOADS.items():
+            if name == w.name:
+                continue
+            steps = max(5, min(args.steps, 200 if ow.flops < 1e9 else args.steps))
+            wm, em = time_workload(fa, torch, ow, steps, args.warmup)
+            r = roofline_for(ow, em, sha)
+            also.append({"workload": name, "B": ow.B, "H": ow.H, "Nq": ow.Nq, "Nk": ow.Nk, "d": ow.d,
+                         "dtype": ow.dtype, "causal": ow.causal, "ms_per_step": round(wm, 4),
+                         "tflops": round(ow.flops / (wm * 1e-3) / 1e12, 2), "roofline": r})
+            log(f"  {name}: {wm:.3f} ms/step, {r['achieved']} TFLOP/s kernel, {100 * r['frac']:.1f}% of {ow.dtype} peak")
+        sweep, copy_gbs = hbm_sweep(fa, torch, args.steps)
+        for s in sweep:
+            log(f"  short N={s['N']}: {s['GB_per_s']} GB/s ({100 * s['hbm_frac']:.1f}% of 8 TB/s)")
+        log(f"  2 GiB device copy: {copy_gbs} GB/s")
+
+    cpu = None
+    if not args.quick and not args.no_cpu:
+        log("cpu baseline (fp64 oracle)...")
+        cpu = cpu_baseline(w)
+        log(f"  {cpu}")
+
+    line = {
+        "metric": "attention fwd TFLOP/s and % of MI355X dtype peak (B4 H4 N4096 d64/d128)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) q, k, v (torch CPU generator, rounded to the dtype), resident in HBM",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} {w.dtype} "
+                               f"{'causal' if w.causal else 'non-causal'} scale={w.softmax_scale:.6g}",
+                   "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
+        "roofline": roofline_for(w, ev_ms, sha),
+        "cpu_baseline": cpu,
+        "also": also,
+        "hbm_sweep": {"runs": sweep, "device_copy_GB_per_s": copy_gbs} if sweep else None,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "kernel_sha": sha,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
