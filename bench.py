@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--workload", default="pages_f32")
     ap.add_argument("--quick", action="store_true", help="headline only: no other workloads, sweep or CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -188,6 +190,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
     fa.ensure_built()
     fa.lib()
     sha = kernel_sha()

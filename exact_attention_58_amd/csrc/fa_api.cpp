@@ -52,18 +52,25 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
 }  // namespace
 
 int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                  int num_cus, TileConfig* out) {
+                  int num_cus, bool aligned, TileConfig* out) {
     (void)Nk;
     (void)causal;
-    (void)num_cus;
     TileConfig c{};
     c.dpad = (int)((d + 31) / 32) * 32;
     c.waves = 4;
     c.br = 32 * c.waves;
-    if (dtype == FA_F32)
+    if (dtype == FA_F32) {
         c.bc = c.dpad > 96 ? 32 : 64;
-    else
+    } else {
         c.bc = 64;
+        // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte
+        // loads and its grid still gives every compute unit a workgroup.
+        const int64_t wgs256 = (Nq + 255) / 256 * B * H;
+        if (aligned && d % 8 == 0 && wgs256 >= num_cus) {
+            c.waves = 8;
+            c.br = 256;
+        }
+    }
     // The grid must stay within the 32-bit launch limit.
     const int64_t n_qtiles = (Nq + c.br - 1) / c.br;
     if (n_qtiles * B * H > INT32_MAX) return FA_EUNSUPPORTED;
@@ -92,7 +99,7 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
     fa::TileConfig cfg;
-    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, num_cus > 0 ? num_cus : 256, &cfg);
+    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, num_cus > 0 ? num_cus : 256, true, &cfg);
     if (rc != FA_OK) return (fa_status)rc;
     if (Br) *Br = cfg.br;
     if (Bc) *Bc = cfg.bc;
@@ -113,14 +120,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
         (uintptr_t)lse % 4 != 0)
         return FA_EINVAL;
 
+    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
+                     (d * esz) % 16 == 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
     fa::TileConfig cfg;
-    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, fa::dev_num_cus(dev), &cfg);
+    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, fa::dev_num_cus(dev), vec, &cfg);
     if (rc != FA_OK) return (fa_status)rc;
-
-    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
-                     (d * esz) % 16 == 0;
     fa::FwdArgs a;
     a.q = q;
     a.k = k;

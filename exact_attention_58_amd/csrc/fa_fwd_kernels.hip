@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -74,6 +76,78 @@ __device__ inline float wave_half_min(float x) {
 __device__ inline float wave_half_sum(float x) {
     u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E), fully unrolled.
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// One online-softmax step on a tile of S^T held as NKB blocks of 32 keys (lane: one query,
+// 16 keys per block): apply the key-tail and causal masks, take the tile's row max in log2
+// units, refresh (m, l, O) when the max grew by more than the threshold, and replace s by
+// the unnormalised weights exp2(s*c - m). Returns the lane's share of the tile's row sum.
+// Unmasked tiles skip the per-element scaling: for c >= 0 the max of s*c is c*max(s), for
+// c < 0 it is c*min(s), and the scale folds into the exp2 argument's FMA.
+template <int NKB, int NDB, bool CAUSAL>
+__device__ inline float softmax_step(f32x16 (&s)[NKB], f32x16 (&oacc)[NDB], float& m_run,
+                                     float& l_run, float c, bool masked, int k0, int Nk, int myq,
+                                     int h32) {
+    float mt, cc;
+    if (masked) {
+        mt = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                const bool ok = key < Nk && (!CAUSAL || key <= myq);
+                const float t = ok ? s[kb][r] * c : kNegInf;
+                s[kb][r] = t;
+                mt = fmaxf(mt, t);
+            }
+        mt = wave_half_max(mt);
+        cc = 1.0f;
+    } else if (c >= 0.0f) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mt = wave_half_max(mx) * c;
+        cc = c;
+    } else {
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][r]);
+        mt = wave_half_min(mx) * c;
+        cc = c;
+    }
+    const float m_cand = fmaxf(m_run, mt);
+    if (__any(m_cand > m_run + kRescaleThreshold)) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
+        m_run = m_cand;
+    }
+    const float nm = -m_run;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], cc, nm));
+            s[kb][r] = pv;
+            lsum += pv;
+        }
+    return lsum;
 }
 
 // ---------------------------------------------------------------- 16-bit types
@@ -137,7 +211,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NW = 4, BR = 32 * NW, BC = 64;
     constexpr int KST = DP + 8;   // K row stride (elements): 16-byte pad, conflict-free b128 reads
-    constexpr int VST = DP + 16;  // V row stride: 32-byte pad, conflict-free transposed reads
+    // V row stride: 4 consecutive rows must start in 4 distinct quarters of the 16 bank groups
+    // (the transposed read serves 4 rows x 4 chunks at once): 20 or 12 chunks for d 128 / 64,
+    // the natural 12 or 4 chunks for d 96 / 32.
+    constexpr int VST = (DP == 128 || DP == 64) ? DP + 32 : DP;
     constexpr int CPR = DP / 8;   // 16-byte chunks per row
     constexpr int CH = BC * CPR / (64 * NW);  // chunks per thread per tile
     static_assert(BC * CPR % (64 * NW) == 0, "tile load split");
@@ -173,7 +250,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int n_tiles = (kv_end + BC - 1) / BC;
 
     u32x4 kreg[CH], vreg[CH];
-    auto load_tile = [&](int j) {
+    auto load_tile = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int chunk = tid + c * 64 * NW;
@@ -182,7 +259,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
             vreg[c] = load_chunk16<VEC>(vg, j * BC + row, col, Nk, d);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int chunk = tid + c * 64 * NW;
@@ -218,69 +295,14 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
             for (int ds = 0; ds < NDS; ++ds) s[kb] = Half<T>::mfma(*(const u32x4*)(kp + ds * 16), qf[ds], s[kb]);
         }
 
-        // ---- masks and tile max (log2 units)
+        // ---- online softmax, then pack P to the 16-bit type
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        float mt;
-        if (masked) {
-            mt = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                    const bool ok = key < Nk && (!CAUSAL || key <= myq);
-                    const float t = ok ? s[kb][r] * c : kNegInf;
-                    s[kb][r] = t;
-                    mt = fmaxf(mt, t);
-                }
-            mt = wave_half_max(mt);
-        } else {
-            float mx = s[0][0];
-            if (c >= 0.0f) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-                mx = wave_half_max(mx);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][r]);
-                mx = wave_half_min(mx);
-            }
-            mt = mx * c;
-        }
-
-        // ---- lazy rescale of the running state
-        const float m_cand = fmaxf(m_run, mt);
-        if (__any(m_cand > m_run + kRescaleThreshold)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-            m_run = m_cand;
-        }
-
-        // ---- P = exp2(S*c - m), row sum, 16-bit pack
+        l_run += softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
         unsigned pk[2][8];
-        float lsum = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float p0, p1;
-                if (masked) {
-                    p0 = __builtin_amdgcn_exp2f(s[kb][r] - m_run);
-                    p1 = __builtin_amdgcn_exp2f(s[kb][r + 1] - m_run);
-                } else {
-                    p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
-                    p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -m_run));
-                }
-                lsum += p0 + p1;
-                pk[kb][r >> 1] = Half<T>::pack2(p0, p1);
-            }
-        l_run += lsum;
+            for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
 
         // ---- O^T += V^T P^T: 4 k-steps of 16 keys
         const int i16 = lane & 15, g16 = (lane >> 4) & 1;
@@ -322,6 +344,241 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
                     if (d0 + 1 < d) og[d0 + 1] = Half<T>::one(o1);
                     if (d0 + 2 < d) og[d0 + 2] = Half<T>::one(o2);
                     if (d0 + 3 < d) og[d0 + 3] = Half<T>::one(o3);
+                }
+            }
+        if (h32 == 0) a.lse[(int64_t)bh * Nq + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------- 16-bit, two-group ping-pong
+
+// LDS row pitches. The LDS serves 256 bytes per clock over 64 four-byte banks, i.e. 16 bank
+// groups of 16 bytes; a b128 read is served 16 lanes at a time and a 64-bit transposed read 32
+// lanes at a time. K fragments read 16 consecutive rows at one 16-byte chunk: an odd pitch (in
+// chunks) puts them in 16 distinct groups. V^T fragments read 4 consecutive rows x 4 aligned
+// chunks: a pitch of 4 or 12 chunks mod 16 puts them in 16 distinct groups. Padding rather
+// than an XOR swizzle keeps every operand address a per-lane base plus an immediate offset.
+template <int DP> struct Pitch {
+    static constexpr int K = DP / 8 + 1;                                         // chunks
+    static constexpr int V = (DP == 128 || DP == 64) ? DP / 8 + 4 : DP / 8;      // chunks
+};
+
+// 16-bit forward kernel for aligned inputs with d % 8 == 0: 8 waves in two groups of four.
+// While one group runs its MFMA phase (S^T_j = K_j Q^T and O^T += V_{j-1}^T P_{j-1}^T) the
+// other runs its softmax phase on S_j; a workgroup barrier separates the phases, so on each
+// SIMD (one wave of each group) the matrix core and the vector ALU work at the same time.
+// K/V tiles are double-buffered in LDS and filled by direct HBM->LDS loads issued two phases
+// before their first use. Tail rows of K/V are clamped to row Nk-1 (finite data, masked).
+template <typename T, int DP, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
+    constexpr int WPG = 4, NWAVE = 2 * WPG;
+    constexpr int BR = 32 * NWAVE, BC = 64;
+    constexpr int DCH = DP / 8;                    // 16-byte data chunks per row
+    constexpr int KP = Pitch<DP>::K, VP = Pitch<DP>::V;
+    constexpr int KTILEB = BC * KP * 16, VTILEB = BC * VP * 16;
+    constexpr int NDS = DP / 16;
+    constexpr int NDB = DP / 32;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KTILEB + 2 * VTILEB];  // K0 K1 V0 V1
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index through readfirstlane: the group branch below is a scalar branch, so
+    // each wave executes only its own group's barriers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const int grp = wave / WPG, wig = wave % WPG;
+
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / n_qtiles;
+    int qt = wg - bh * n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int q0 = qt * BR;
+    const int r0w = q0 + grp * 32 * WPG + wig * 32;
+    const int myq = r0w + l32;
+
+    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
+    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
+    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+
+    u32x4 qf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = load_chunk16<true>(qg, myq, ds * 16 + 8 * h32, Nq, d);
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
+    const int n = (kv_end + BC - 1) / BC;
+    // this wave's last tile with a visible key (causal: tiles past the diagonal are skipped)
+    const int last = CAUSAL ? min(n - 1, (r0w + 31) / BC) : n - 1;
+    const int dchunks = d / 8;
+
+    // Direct HBM->LDS load of one K or V tile into rows of PITCH chunks: wave instruction idx
+    // fills LDS chunks [64*idx, 64*idx+64) (wave-uniform destination, lane i -> +16*i); lanes
+    // on padding chunks are masked off. Rows past Nk repeat row Nk-1 (finite; their scores are
+    // masked and their weights are zero).
+    auto issue_tile = [&](auto pitch_c, const uint16_t* src, int tile, uint8_t* dst) __attribute__((always_inline)) {
+        constexpr int PITCH = decltype(pitch_c)::value;
+#pragma unroll
+        for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
+            const int idx = it * NWAVE + wave;
+            if (idx < PITCH) {
+                const int p = idx * 64 + lane;
+                const int r = p / PITCH, cch = p - r * PITCH;
+                const int gr = min(tile * BC + r, Nk - 1);
+                // chunks past d (DP > d) repeat the row's last data chunk: finite, and Q is
+                // zero there, so they add nothing to the scores
+                const int gc = min(cch, dchunks - 1) * 8;
+                if (cch < DCH)
+                    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)gr * d + gc),
+                                                     (FA_LDS void*)(dst + idx * 1024), 16, 0, 0);
+            }
+        }
+    };
+    auto kbuf = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * KTILEB; };
+    auto vbuf = [&](int j) __attribute__((always_inline)) { return smem + 2 * KTILEB + (j & 1) * VTILEB; };
+    using kpc = std::integral_constant<int, KP>;
+    using vpc = std::integral_constant<int, VP>;
+    auto issue_stage = [&](int m) __attribute__((always_inline)) {  // K_{m+1} and V_m
+        if (m + 1 < n) issue_tile(kpc{}, kg, m + 1, kbuf(m + 1));
+        if (m < n) issue_tile(vpc{}, vg, m, vbuf(m));
+    };
+    auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+    float m_run = kNegInf, l_run = 0.0f;
+    const float c = a.scale_log2;
+    f32x16 s[2];
+    unsigned pk[2][8];
+
+    // MFMA phase as one unrolled micro-program: NQ MFMAs of S^T_j = K_j Q^T (k-step ds of key
+    // block kb) then NP MFMAs of O^T += V_{j-1}^T P_{j-1}^T (key step t of head-dim block db).
+    // Each MFMA's LDS operand is read LA MFMAs ahead into a small ring, and scheduling
+    // barriers keep that order, so the one wave of this group on the SIMD keeps the matrix
+    // core fed while the LDS reads of the next MFMAs are in flight. A QK operand is one b128
+    // read, a PV operand two transposed b64 reads: at most 2*LA LDS reads are outstanding.
+    constexpr int NQ = 2 * NDS, NP = (BC / 16) * NDB, LA = DP >= 128 ? 4 : 6;
+    const int i16 = lane & 15, g16 = (lane >> 4) & 1;
+    // per-lane operand bases; every fragment is base + compile-time offset
+    const int kbase = l32 * KP * 16 + h32 * 16;
+    const int vbase = (4 * h32 + (i16 >> 2)) * VP * 16 + (16 * g16 + 4 * (i16 & 3)) * 2;
+    auto fetch = [&](auto ic, const uint8_t* kb_, const uint8_t* vb_) __attribute__((always_inline)) -> u32x4 {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i < NQ) {
+            constexpr int ds = i >> 1, kb = i & 1;
+            return *(const u32x4*)(kb_ + kbase + kb * 32 * KP * 16 + ds * 32);
+        } else {
+            constexpr int pi = i - NQ, t = pi / NDB, db = pi % NDB;
+            const uint8_t* vp = vb_ + vbase + t * 16 * VP * 16 + db * 64;
+            const u32x2 lo = lds_read_tr16((const uint16_t*)vp);
+            const u32x2 hi = lds_read_tr16((const uint16_t*)(vp + 8 * VP * 16));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+    // DO_QK: compute S^T_j; DO_PV: accumulate P V of tile jp. Both are compile-time so the
+    // unrolled program and its operand ring are static.
+    auto mphase_t = [&](auto do_qk_c, auto do_pv_c, int j, int jp) __attribute__((always_inline)) {
+        constexpr bool DO_QK = decltype(do_qk_c)::value, DO_PV = decltype(do_pv_c)::value;
+        constexpr int first = DO_QK ? 0 : NQ, end = DO_PV ? NQ + NP : NQ;
+        const uint8_t* kb_ = kbuf(j);
+        const uint8_t* vb_ = vbuf(jp);
+        if (DO_QK) {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+        }
+        u32x4 ring[LA];
+        static_for<0, LA>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (first + i < end) ring[i] = fetch(std::integral_constant<int, first + i>{}, kb_, vb_);
+        });
+        static_for<first, end>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int slot = (i - first) % LA;
+            const u32x4 op = ring[slot];
+            if constexpr (i + LA < end) ring[slot] = fetch(std::integral_constant<int, i + LA>{}, kb_, vb_);
+            if constexpr (i < NQ) {
+                constexpr int ds = i >> 1, kb = i & 1;
+                s[kb] = Half<T>::mfma(op, qf[ds], s[kb]);
+            } else {
+                constexpr int pi = i - NQ, t = pi / NDB, db = pi % NDB;
+                const u32x4 pb = {pk[t >> 1][4 * (t & 1) + 0], pk[t >> 1][4 * (t & 1) + 1],
+                                  pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
+                oacc[db] = Half<T>::mfma(op, pb, oacc[db]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    auto mphase = [&](bool do_qk, int j, bool do_pv, int jp) __attribute__((always_inline)) {
+        if (do_qk && do_pv) mphase_t(yes{}, yes{}, j, jp);
+        else if (do_qk) mphase_t(yes{}, no{}, j, jp);
+        else if (do_pv) mphase_t(no{}, yes{}, j, jp);
+    };
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+        const int k0 = j * BC;
+        const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
+        l_run += softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
+    };
+
+    // prologue: K_0 resident before the first MFMA phase
+    issue_tile(kpc{}, kg, 0, kbuf(0));
+    wait_loads();
+    __syncthreads();
+
+    if (grp == 0) {
+        for (int j = 0; j < n; ++j) {
+            // MFMA phase (global phase 2j)
+            issue_stage(j);
+            mphase(j <= last, j, j > 0 && j - 1 <= last, j - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            // softmax phase (global phase 2j+1)
+            if (j <= last) softmax(j);
+            wait_loads();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        }
+        mphase(false, n - 1, n - 1 <= last, n - 1);
+        __syncthreads();
+    } else {
+        issue_stage(0);
+        __syncthreads();
+        for (int j = 0; j < n; ++j) {
+            // MFMA phase (global phase 2j+1)
+            mphase(j <= last, j, j > 0 && j - 1 <= last, j - 1);
+            wait_loads();
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            // softmax phase (global phase 2j+2)
+            issue_stage(j + 1);
+            if (j <= last) softmax(j);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+        }
+        mphase(false, n - 1, n - 1 <= last, n - 1);
+    }
+
+    // epilogue: O = O / l, L = (m + log2 l) ln 2
+    const float l_tot = wave_half_sum(l_run);
+    const float inv = 1.0f / l_tot;
+    if (myq < Nq) {
+        uint16_t* og = (uint16_t*)a.o + ((int64_t)bh * Nq + myq) * d;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * h32;
+                if (d0 < d) {
+                    u32x2 w = {Half<T>::pack2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv),
+                               Half<T>::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
+                    *(u32x2*)(og + d0) = w;
                 }
             }
         if (h32 == 0) a.lse[(int64_t)bh * Nq + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -396,7 +653,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const int n_tiles = (kv_end + BC - 1) / BC;
 
     f32x4 kreg[CH], vreg[CH];
-    auto load_tile = [&](int j) {
+    auto load_tile = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
             const int chunk = tid + cc * 64 * NW;
@@ -405,7 +662,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
             vreg[cc] = load_chunk32<VEC>(vg, j * BC + row, col, Nk, d);
         }
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
             const int chunk = tid + cc * 64 * NW;
@@ -446,58 +703,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
         }
 
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        float mt;
-        if (masked) {
-            mt = kNegInf;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                    const bool ok = key < Nk && (!CAUSAL || key <= myq);
-                    const float t = ok ? s[kb][r] * c : kNegInf;
-                    s[kb][r] = t;
-                    mt = fmaxf(mt, t);
-                }
-            mt = wave_half_max(mt);
-        } else {
-            float mx = s[0][0];
-            if (c >= 0.0f) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-                mx = wave_half_max(mx);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][r]);
-                mx = wave_half_min(mx);
-            }
-            mt = mx * c;
-        }
-
-        const float m_cand = fmaxf(m_run, mt);
-        if (__any(m_cand > m_run + kRescaleThreshold)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) oacc[i] *= alpha;
-            m_run = m_cand;
-        }
-
-        float lsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = masked ? __builtin_amdgcn_exp2f(s[kb][r] - m_run)
-                                       : __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_run));
-                s[kb][r] = p;
-                lsum += p;
-            }
-        l_run += lsum;
+        l_run += softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
 
         // O^T += V^T P^T, one key per lane half per MFMA: k-step r of block kb is
         // key kb*32 + 8*(r/4) + 4*h32 + r%4, the key the lane's S^T register r holds.
@@ -539,31 +745,35 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
 // ---------------------------------------------------------------- launch
 
 template <typename K>
-static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st) {
+static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st, int threads) {
     const int n_qtiles = (a.Nq + br - 1) / br;
     const int64_t total = (int64_t)n_qtiles * a.B * a.H;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(256), 0, st, a, n_qtiles);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(threads), 0, st, a, n_qtiles);
     return (int)hipGetLastError();
 }
 
 template <typename T, int DP>
-static int launch16(const FwdArgs& a, bool vec, hipStream_t st) {
-    if (a.causal) {
-        return vec ? launch(fwd16_kernel<T, DP, true, true>, a, 128, st)
-                   : launch(fwd16_kernel<T, DP, true, false>, a, 128, st);
+static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
+    if (cfg.waves == 8) {  // aligned, d % 8 == 0 (checked by the caller)
+        if (a.causal) return launch(fwd16_pp_kernel<T, DP, true>, a, cfg.br, st, 512);
+        return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
     }
-    return vec ? launch(fwd16_kernel<T, DP, false, true>, a, 128, st)
-               : launch(fwd16_kernel<T, DP, false, false>, a, 128, st);
+    if (a.causal) {
+        return vec ? launch(fwd16_kernel<T, DP, true, true>, a, 128, st, 256)
+                   : launch(fwd16_kernel<T, DP, true, false>, a, 128, st, 256);
+    }
+    return vec ? launch(fwd16_kernel<T, DP, false, true>, a, 128, st, 256)
+               : launch(fwd16_kernel<T, DP, false, false>, a, 128, st, 256);
 }
 
 template <int DP, int BC>
 static int launch32(const FwdArgs& a, bool vec, hipStream_t st) {
     if (a.causal) {
-        return vec ? launch(fwd32_kernel<DP, BC, true, true>, a, 128, st)
-                   : launch(fwd32_kernel<DP, BC, true, false>, a, 128, st);
+        return vec ? launch(fwd32_kernel<DP, BC, true, true>, a, 128, st, 256)
+                   : launch(fwd32_kernel<DP, BC, true, false>, a, 128, st, 256);
     }
-    return vec ? launch(fwd32_kernel<DP, BC, false, true>, a, 128, st)
-               : launch(fwd32_kernel<DP, BC, false, false>, a, 128, st);
+    return vec ? launch(fwd32_kernel<DP, BC, false, true>, a, 128, st, 256)
+               : launch(fwd32_kernel<DP, BC, false, false>, a, 128, st, 256);
 }
 
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) {
@@ -571,10 +781,10 @@ int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) 
     if (a.dtype == 2 || a.dtype == 1) {
         const bool bf = a.dtype == 2;
         switch (cfg.dpad) {
-            case 32: return bf ? launch16<__bf16, 32>(a, vec, st) : launch16<_Float16, 32>(a, vec, st);
-            case 64: return bf ? launch16<__bf16, 64>(a, vec, st) : launch16<_Float16, 64>(a, vec, st);
-            case 96: return bf ? launch16<__bf16, 96>(a, vec, st) : launch16<_Float16, 96>(a, vec, st);
-            case 128: return bf ? launch16<__bf16, 128>(a, vec, st) : launch16<_Float16, 128>(a, vec, st);
+            case 32: return bf ? launch16<__bf16, 32>(a, cfg, vec, st) : launch16<_Float16, 32>(a, cfg, vec, st);
+            case 64: return bf ? launch16<__bf16, 64>(a, cfg, vec, st) : launch16<_Float16, 64>(a, cfg, vec, st);
+            case 96: return bf ? launch16<__bf16, 96>(a, cfg, vec, st) : launch16<_Float16, 96>(a, cfg, vec, st);
+            case 128: return bf ? launch16<__bf16, 128>(a, cfg, vec, st) : launch16<_Float16, 128>(a, cfg, vec, st);
             default: return (int)hipErrorInvalidValue;
         }
     }

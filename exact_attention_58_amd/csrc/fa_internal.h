@@ -28,8 +28,9 @@ struct TileConfig {
 };
 
 // Pure selection logic (no HIP calls). Returns 0 on success, 2 if no kernel fits.
+// `aligned`: all buffers 16-byte aligned and d*element_size a multiple of 16.
 int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                  int causal, int num_cus, TileConfig* out);
+                  int causal, int num_cus, bool aligned, TileConfig* out);
 
 // Launches the kernel for `cfg` on `stream`; returns the hipError_t of the launch as int.
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream);

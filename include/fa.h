@@ -95,7 +95,9 @@ const char* fa_status_str(fa_status s);
  * the padded head dimension the kernel is compiled for (*dpad). Any output
  * pointer may be NULL. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
  * `num_cus` is the device's compute-unit count (256 on MI355X); it only
- * affects the query-tile height when the grid would not fill the chip.
+ * affects the query-tile height when the grid would not fill the chip. The
+ * answer assumes 16-byte aligned buffers; fa_fwd on unaligned buffers (or a
+ * 16-bit d that is not a multiple of 8) uses the 4-wave, 128-row kernel.
  */
 fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                            int64_t d, int causal, int num_cus,

@@ -75,11 +75,30 @@ def test_select_config(dtype, d):
     assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
     assert cfg["Br"] == 32 * cfg["waves"]
     assert cfg["Bc"] in (32, 64)
-    # LDS of the chosen tiles (K with a 16-byte row pad, V padded for its read pattern)
     s = 4 if dtype == "f32" else 2
-    vpad = 0 if dtype == "f32" else 32
-    lds = cfg["Bc"] * (cfg["dpad"] * s + 16) + cfg["Bc"] * (cfg["dpad"] * s + vpad)
-    assert lds * 2 <= 160 * 1024  # two workgroups per CU fit the 160 KiB LDS
+    if cfg["waves"] == 8:
+        # ping-pong kernel: double-buffered, swizzled K and V tiles (96-wide rows padded to 128),
+        # one workgroup per CU
+        assert dtype != "f32" and d % 8 == 0
+        pitch = 256 if cfg["dpad"] > 64 else cfg["dpad"] * s
+        lds = 4 * cfg["Bc"] * pitch
+        assert lds <= 160 * 1024
+    else:
+        # 4-wave kernel: K with a 16-byte row pad, V padded for its transposed reads
+        vpad = 64 if (dtype != "f32" and cfg["dpad"] in (64, 128)) else 0
+        lds = cfg["Bc"] * (cfg["dpad"] * s + 16) + cfg["Bc"] * (cfg["dpad"] * s + vpad)
+        assert lds * 2 <= 160 * 1024  # two workgroups per CU fit the 160 KiB LDS
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_select_config_grid_fill(dtype):
+    """The 256-row kernel only when its grid gives every compute unit a workgroup."""
+    big = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 128, False, num_cus=256)
+    assert big["waves"] == 8 and big["Br"] == 256
+    small = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, False, num_cus=256)
+    assert small["waves"] == 4 and small["Br"] == 128
+    odd_d = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 100, False, num_cus=256)
+    assert odd_d["waves"] == 4
 
 
 def test_select_config_errors():
