@@ -23,7 +23,7 @@
 //    of one head-dim column.
 //  * The online softmax uses exp2 with the scale folded into log2(e) (page "Add
 //    Fused Multi-Head Attention example"); P is rounded to the input type for
-//    the PV product while l sums the fp32 P.
+//    the PV product while l sums the fp32 weights. The fp32 path keeps P in fp32.
 //  * K/V tiles are loaded from HBM with 16-byte coalesced loads into registers
 //    one tile ahead of their use and stored to LDS behind a barrier.
 //  * Keys past Nk are zero in LDS and masked to -inf; the causal mask keeps key
@@ -87,48 +87,67 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
     }
 }
 
-// One online-softmax step on a tile of S^T held as NKB blocks of 32 keys (lane: one query,
-// 16 keys per block): apply the key-tail and causal masks, take the tile's row max in log2
-// units, refresh (m, l, O) when the max grew by more than the threshold, and replace s by
-// the unnormalised weights exp2(s*c - m). Returns the lane's share of the tile's row sum.
-// Unmasked tiles skip the per-element scaling: for c >= 0 the max of s*c is c*max(s), for
-// c < 0 it is c*min(s), and the scale folds into the exp2 argument's FMA.
-template <int NKB, int NDB, bool CAUSAL>
-__device__ inline float softmax_step(f32x16 (&s)[NKB], f32x16 (&oacc)[NDB], float& m_run,
-                                     float& l_run, float c, bool masked, int k0, int Nk, int myq,
-                                     int h32) {
-    float mt, cc;
+// Maximum of the NKB*16 values of s as a balanced tree (v_max3), so the dependency chain is
+// logarithmic in the number of values instead of linear. MIN selects the minimum instead.
+template <int NKB, bool MIN>
+__device__ __attribute__((always_inline)) inline float tile_extreme(const f32x16 (&s)[NKB]) {
+    float v[NKB * 16];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[kb * 16 + r] = s[kb][r];
+    int n = NKB * 16;
+#pragma unroll
+    for (int step = 0; step < 6; ++step) {
+        if (n == 1) break;
+        const int m = (n + 2) / 3;
+#pragma unroll
+        for (int i = 0; i < m; ++i) {
+            const float a = v[3 * i];
+            const float b = 3 * i + 1 < n ? v[3 * i + 1] : a;
+            const float c = 3 * i + 2 < n ? v[3 * i + 2] : a;
+            v[i] = MIN ? fminf(fminf(a, b), c) : fmaxf(fmaxf(a, b), c);
+        }
+        n = m;
+    }
+    return v[0];
+}
+
+// First half of an online-softmax step on a tile of S^T held as NKB blocks of 32 keys (lane:
+// one query, 16 keys per block): apply the key-tail and causal masks and return the tile's
+// row max in log2 units; *cc receives the factor that turns s into log2 units (the scale for
+// unmasked tiles, 1 for masked tiles, whose s this function scales in place). Unmasked
+// tiles skip the per-element scaling: for c >= 0 the max of s*c is c*max(s), for c < 0 it
+// is c*min(s), and the scale folds into the exp2 argument's FMA.
+template <int NKB, bool CAUSAL>
+__device__ __attribute__((always_inline)) inline float tile_max_log2(f32x16 (&s)[NKB], float c, bool masked,
+                                                                     int k0, int Nk, int myq, int h32,
+                                                                     float* cc) {
     if (masked) {
-        mt = kNegInf;
+        // key = k0 + 4*h32 + off with a compile-time offset per register: visible iff
+        // key <= Nk - 1 and (causal) key <= myq, i.e. off <= lim
+        const int lim = (CAUSAL ? min(Nk - 1, myq) : Nk - 1) - k0 - 4 * h32;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                const bool ok = key < Nk && (!CAUSAL || key <= myq);
-                const float t = ok ? s[kb][r] * c : kNegInf;
-                s[kb][r] = t;
-                mt = fmaxf(mt, t);
+                const int off = kb * 32 + 8 * (r >> 2) + (r & 3);
+                s[kb][r] = off <= lim ? s[kb][r] * c : kNegInf;
             }
-        mt = wave_half_max(mt);
-        cc = 1.0f;
-    } else if (c >= 0.0f) {
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mt = wave_half_max(mx) * c;
-        cc = c;
-    } else {
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fminf(mx, s[kb][r]);
-        mt = wave_half_min(mx) * c;
-        cc = c;
+        *cc = 1.0f;
+        return wave_half_max(tile_extreme<NKB, false>(s));
     }
+    *cc = c;
+    if (c >= 0.0f) return wave_half_max(tile_extreme<NKB, false>(s)) * c;
+    return wave_half_min(tile_extreme<NKB, true>(s)) * c;
+}
+
+// Second half: refresh (m, l, O) when the row max grew by more than the threshold, then
+// replace s by the unnormalised weights exp2(s*cc - m). The caller adds the weights to l.
+template <int NKB, int NDB>
+__device__ __attribute__((always_inline)) inline void tile_exp(f32x16 (&s)[NKB], f32x16 (&oacc)[NDB],
+                                                               float& m_run, float& l_run, float mt,
+                                                               float cc) {
     const float m_cand = fmaxf(m_run, mt);
     if (__any(m_cand > m_run + kRescaleThreshold)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
@@ -138,16 +157,35 @@ __device__ inline float softmax_step(f32x16 (&s)[NKB], f32x16 (&oacc)[NDB], floa
         m_run = m_cand;
     }
     const float nm = -m_run;
-    float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], cc, nm));
-            s[kb][r] = pv;
-            lsum += pv;
-        }
-    return lsum;
+        for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], cc, nm));
+}
+
+// Whole online-softmax step (masks, max, rescale, exp) for kernels that run it in one place.
+template <int NKB, int NDB, bool CAUSAL>
+__device__ __attribute__((always_inline)) inline void softmax_step(
+        f32x16 (&s)[NKB], f32x16 (&oacc)[NDB], float& m_run, float& l_run, float c, bool masked,
+        int k0, int Nk, int myq, int h32) {
+    float cc;
+    const float mt = tile_max_log2<NKB, CAUSAL>(s, c, masked, k0, Nk, myq, h32, &cc);
+    tile_exp<NKB, NDB>(s, oacc, m_run, l_run, mt, cc);
+}
+
+// Sum of the weights of a tile as a balanced tree (fp32 path).
+template <int NKB>
+__device__ __attribute__((always_inline)) inline float tile_sum(const f32x16 (&s)[NKB]) {
+    float v[NKB * 16];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[kb * 16 + r] = s[kb][r];
+#pragma unroll
+    for (int n = NKB * 16; n > 1; n /= 2)
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+    return v[0];
 }
 
 // ---------------------------------------------------------------- 16-bit types
@@ -178,9 +216,55 @@ template <> struct Half<_Float16> {
     static __device__ inline uint16_t one(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
 };
 
+// Packs the tile's weights to the 16-bit type (pk[kb][r/2] holds keys r, r+1 of block kb) and
+// returns the sum of the fp32 weights (a balanced tree). l sums the fp32 weights, not the
+// rounded ones: a 16-bit weight carries up to 2^-8 relative rounding error, which a row with
+// few visible keys would pass straight into L = m + ln(l).
+template <typename T>
+__device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16 (&s)[2], unsigned (&pk)[2][8]) {
+    const float sum = tile_sum<2>(s);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
+    return sum;
+}
+
 __device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
     i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
     return __builtin_bit_cast(u32x2, t);
+}
+
+// LDS reads issued through inline asm, for kernels that also fill LDS with direct HBM->LDS
+// loads: the compiler cannot prove that a read does not alias an in-flight load and would
+// otherwise wait for every outstanding load before each LDS read. The kernel's own barrier
+// schedule guarantees that the buffers read are not being written, and the reads' completion
+// is awaited explicitly (lgkm_wait) with a count known at compile time.
+template <int OFF>
+__device__ inline u32x4 lds_rd128(unsigned addr) {
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+template <int OFF>
+__device__ inline u32x2 lds_rdtr16(unsigned addr) {
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+// Waits until at most N LDS/scalar-memory operations are outstanding; tied to `x` so that
+// the consumer of x cannot be scheduled above the wait.
+template <int N>
+__device__ inline void lgkm_wait(u32x4& x) {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+// Workgroup barrier without the memory fence __syncthreads() adds: that fence waits for every
+// outstanding HBM->LDS load of the issuing wave. Kernels using it order LDS traffic
+// themselves: loads are awaited with an explicit s_waitcnt vmcnt(0) one phase later, and LDS
+// reads are awaited before their results are used.
+__device__ inline void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+__device__ inline unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const FA_LDS void*)(p);
 }
 
 // One 16-byte chunk (8 elements) of row `row`, columns [col, col+8), zero outside
@@ -297,12 +381,9 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
 
         // ---- online softmax, then pack P to the 16-bit type
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        l_run += softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+        softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
         unsigned pk[2][8];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
+        l_run += pack_and_sum<T>(s, pk);
 
         // ---- O^T += V^T P^T: 4 k-steps of 16 keys
         const int i16 = lane & 15, g16 = (lane >> 4) & 1;
@@ -364,11 +445,26 @@ template <int DP> struct Pitch {
 };
 
 // 16-bit forward kernel for aligned inputs with d % 8 == 0: 8 waves in two groups of four.
-// While one group runs its MFMA phase (S^T_j = K_j Q^T and O^T += V_{j-1}^T P_{j-1}^T) the
-// other runs its softmax phase on S_j; a workgroup barrier separates the phases, so on each
-// SIMD (one wave of each group) the matrix core and the vector ALU work at the same time.
-// K/V tiles are double-buffered in LDS and filled by direct HBM->LDS loads issued two phases
-// before their first use. Tail rows of K/V are clamped to row Nk-1 (finite data, masked).
+// While one group runs its MFMA phase the other runs its softmax phase; a workgroup barrier
+// separates the phases, so on each SIMD (one wave of each group) the matrix core and the
+// vector ALU work at the same time. Global phase 2m is group 0's MFMA phase m and group 1's
+// softmax phase m-1; phase 2m+1 is group 1's MFMA phase m and group 0's softmax phase m.
+//  * MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T. Around the MFMAs the
+//    wave also folds the fp32 weights of tile j-1 into l, issues the direct HBM->LDS loads
+//    of K_{j+2} and V_{j+2} (its share), and after the last MFMA applies the masks and takes
+//    the row max of S_j.
+//  * Softmax phase j: the rescale test, exp2 of the tile, packing P_j to 16 bits, and the
+//    first PV operands of the next MFMA phase (read ahead of the barrier).
+// The vector work left in the softmax phase is what the PV product waits for; the rest runs
+// in the gaps of the MFMA phase. Each wave awaits its loads at the start of its next MFMA
+// phase, before the end of global phase 2j+3. K has three LDS buffers (K_j is read in MFMA
+// phase j), V four (V_j is read at the end of softmax phase j and in MFMA phase j+1), so no
+// buffer is rewritten while either group may still read it. Tail rows of K/V are clamped to
+// row Nk-1. Both groups run one loop body (their differences are scalar flags), so the
+// accumulators keep fixed registers. Every MFMA phase runs the full program: the first one
+// multiplies a zero P by the resident V_0, and a causal wave past its diagonal runs fully
+// masked tiles whose weights are exactly zero; the phases are barrier-bound, so neither
+// costs time.
 template <typename T, int DP, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
@@ -380,7 +476,8 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NDS = DP / 16;
     constexpr int NDB = DP / 32;
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KTILEB + 2 * VTILEB];  // K0 K1 V0 V1
+    constexpr int NKBUF = 3, NVBUF = 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NKBUF * KTILEB + NVBUF * VTILEB];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index through readfirstlane: the group branch below is a scalar branch, so
@@ -409,39 +506,66 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
     const int n = (kv_end + BC - 1) / BC;
-    // this wave's last tile with a visible key (causal: tiles past the diagonal are skipped)
-    const int last = CAUSAL ? min(n - 1, (r0w + 31) / BC) : n - 1;
     const int dchunks = d / 8;
 
     // Direct HBM->LDS load of one K or V tile into rows of PITCH chunks: wave instruction idx
     // fills LDS chunks [64*idx, 64*idx+64) (wave-uniform destination, lane i -> +16*i); lanes
-    // on padding chunks are masked off. Rows past Nk repeat row Nk-1 (finite; their scores are
-    // masked and their weights are zero).
-    auto issue_tile = [&](auto pitch_c, const uint16_t* src, int tile, uint8_t* dst) __attribute__((always_inline)) {
+    // on padding chunks are masked off. The lane's source offset within a full tile is fixed,
+    // so it is computed once (slot_off; -1 = padding lane). A tile that runs past Nk repeats
+    // row Nk-1 in its tail rows (finite; their scores are masked and their weights are zero).
+    constexpr int KIT = (KP + NWAVE - 1) / NWAVE, VIT = (VP + NWAVE - 1) / NWAVE;
+    int koff[KIT], voff[VIT];
+    auto init_slots = [&](auto pitch_c, int* off) __attribute__((always_inline)) {
         constexpr int PITCH = decltype(pitch_c)::value;
 #pragma unroll
         for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
             const int idx = it * NWAVE + wave;
-            if (idx < PITCH) {
-                const int p = idx * 64 + lane;
-                const int r = p / PITCH, cch = p - r * PITCH;
-                const int gr = min(tile * BC + r, Nk - 1);
-                // chunks past d (DP > d) repeat the row's last data chunk: finite, and Q is
-                // zero there, so they add nothing to the scores
-                const int gc = min(cch, dchunks - 1) * 8;
-                if (cch < DCH)
-                    __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)gr * d + gc),
+            const int p = idx * 64 + lane;
+            const int r = p / PITCH, cch = p - r * PITCH;
+            off[it] = (idx < PITCH && cch < DCH) ? (r * d + min(cch, dchunks - 1) * 8) * 2 : -1;
+        }
+    };
+    auto issue_tile = [&](auto pitch_c, const uint16_t* src, int tile, uint8_t* dst, const int* off)
+                          __attribute__((always_inline)) {
+        constexpr int PITCH = decltype(pitch_c)::value;
+        if (tile * BC + BC <= Nk) {
+            const uint8_t* base = (const uint8_t*)(src + (int64_t)tile * BC * d);
+#pragma unroll
+            for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
+                const int idx = it * NWAVE + wave;
+                if (idx < PITCH && off[it] >= 0)
+                    __builtin_amdgcn_global_load_lds((const void*)(base + off[it]),
                                                      (FA_LDS void*)(dst + idx * 1024), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
+                const int idx = it * NWAVE + wave;
+                if (idx < PITCH) {
+                    const int p = idx * 64 + lane;
+                    const int r = p / PITCH, cch = p - r * PITCH;
+                    const int gr = min(tile * BC + r, Nk - 1);
+                    // chunks past d (DP > d) repeat the row's last data chunk: finite, and Q
+                    // is zero there, so they add nothing to the scores
+                    const int gc = min(cch, dchunks - 1) * 8;
+                    if (cch < DCH)
+                        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)gr * d + gc),
+                                                         (FA_LDS void*)(dst + idx * 1024), 16, 0, 0);
+                }
             }
         }
     };
-    auto kbuf = [&](int j) __attribute__((always_inline)) { return smem + (j & 1) * KTILEB; };
-    auto vbuf = [&](int j) __attribute__((always_inline)) { return smem + 2 * KTILEB + (j & 1) * VTILEB; };
+    auto kbuf = [&](int j) __attribute__((always_inline)) { return smem + (j % NKBUF) * KTILEB; };
+    auto vbuf = [&](int j) __attribute__((always_inline)) { return smem + NKBUF * KTILEB + (j % NVBUF) * VTILEB; };
     using kpc = std::integral_constant<int, KP>;
     using vpc = std::integral_constant<int, VP>;
-    auto issue_stage = [&](int m) __attribute__((always_inline)) {  // K_{m+1} and V_m
-        if (m + 1 < n) issue_tile(kpc{}, kg, m + 1, kbuf(m + 1));
-        if (m < n) issue_tile(vpc{}, vg, m, vbuf(m));
+    init_slots(kpc{}, koff);
+    init_slots(vpc{}, voff);
+    auto issue_tiles = [&](int m) __attribute__((always_inline)) {  // K_m and V_m
+        if (m < n) {
+            issue_tile(kpc{}, kg, m, kbuf(m), koff);
+            issue_tile(vpc{}, vg, m, vbuf(m), voff);
+        }
     };
     auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -452,6 +576,8 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const float c = a.scale_log2;
     f32x16 s[2];
     unsigned pk[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk[0][i] = pk[1][i] = 0u;
 
     // MFMA phase as one unrolled micro-program: NQ MFMAs of S^T_j = K_j Q^T (k-step ds of key
     // block kb) then NP MFMAs of O^T += V_{j-1}^T P_{j-1}^T (key step t of head-dim block db).
@@ -459,111 +585,143 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     // barriers keep that order, so the one wave of this group on the SIMD keeps the matrix
     // core fed while the LDS reads of the next MFMAs are in flight. A QK operand is one b128
     // read, a PV operand two transposed b64 reads: at most 2*LA LDS reads are outstanding.
-    constexpr int NQ = 2 * NDS, NP = (BC / 16) * NDB, LA = DP >= 128 ? 4 : 6;
+    constexpr int NQ = 2 * NDS, NP = (BC / 16) * NDB;
+    constexpr int LA = 6;
     const int i16 = lane & 15, g16 = (lane >> 4) & 1;
-    // per-lane operand bases; every fragment is base + compile-time offset
-    const int kbase = l32 * KP * 16 + h32 * 16;
-    const int vbase = (4 * h32 + (i16 >> 2)) * VP * 16 + (16 * g16 + 4 * (i16 & 3)) * 2;
-    auto fetch = [&](auto ic, const uint8_t* kb_, const uint8_t* vb_) __attribute__((always_inline)) -> u32x4 {
+    // per-lane operand bases (LDS byte addresses); every fragment is base + compile-time offset
+    const unsigned kbase = l32 * KP * 16 + h32 * 16;
+    const unsigned vbase = (4 * h32 + (i16 >> 2)) * VP * 16 + (16 * g16 + 4 * (i16 & 3)) * 2;
+    const unsigned smem_a = lds_addr(smem);
+    auto kaddr = [&](int j) __attribute__((always_inline)) { return smem_a + (j % NKBUF) * KTILEB + kbase; };
+    auto vaddr = [&](int j) __attribute__((always_inline)) { return smem_a + NKBUF * KTILEB + (j % NVBUF) * VTILEB + vbase; };
+    auto fetch = [&](auto ic, unsigned ka, unsigned va) __attribute__((always_inline)) -> u32x4 {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i < NQ) {
-            constexpr int ds = i >> 1, kb = i & 1;
-            return *(const u32x4*)(kb_ + kbase + kb * 32 * KP * 16 + ds * 32);
-        } else {
-            constexpr int pi = i - NQ, t = pi / NDB, db = pi % NDB;
-            const uint8_t* vp = vb_ + vbase + t * 16 * VP * 16 + db * 64;
-            const u32x2 lo = lds_read_tr16((const uint16_t*)vp);
-            const u32x2 hi = lds_read_tr16((const uint16_t*)(vp + 8 * VP * 16));
+        if constexpr (i < NP) {
+            constexpr int t = i / NDB, db = i % NDB;
+            constexpr int off = t * 16 * VP * 16 + db * 64;
+            const u32x2 lo = lds_rdtr16<off>(va);
+            const u32x2 hi = lds_rdtr16<off + 8 * VP * 16>(va);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            constexpr int qi = i - NP, ds = qi >> 1, kb = qi & 1;
+            return lds_rd128<kb * 32 * KP * 16 + ds * 32>(ka);
         }
     };
-    // DO_QK: compute S^T_j; DO_PV: accumulate P V of tile jp. Both are compile-time so the
-    // unrolled program and its operand ring are static.
+    u32x4 ring[LA];
+    // first operands of the PV product on tile jp (at most LA, all of them V fragments),
+    // read before the MFMA phase starts
+    constexpr int NPRE = LA < NP ? LA : NP;
+    auto prefetch_pv = [&](int jp) __attribute__((always_inline)) {
+        const unsigned va = vaddr(jp);
+        static_for<0, NPRE>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            ring[i] = fetch(std::integral_constant<int, i>{}, 0u, va);
+        });
+    };
+    // DO_PV: accumulate P V of tile jp (its first LA operands already in the ring);
+    // DO_QK: compute S^T_j. Both compile-time so the unrolled program and its ring are static.
+    // partial sums of the previous tile's weights (tree folded around the MFMAs)
+    float part[16];
     auto mphase_t = [&](auto do_qk_c, auto do_pv_c, int j, int jp) __attribute__((always_inline)) {
         constexpr bool DO_QK = decltype(do_qk_c)::value, DO_PV = decltype(do_pv_c)::value;
-        constexpr int first = DO_QK ? 0 : NQ, end = DO_PV ? NQ + NP : NQ;
-        const uint8_t* kb_ = kbuf(j);
-        const uint8_t* vb_ = vbuf(jp);
-        if (DO_QK) {
-            s[0] = f32x16{};
-            s[1] = f32x16{};
-        }
-        u32x4 ring[LA];
-        static_for<0, LA>([&](auto ic) __attribute__((always_inline)) {
+        static_assert(DO_PV, "the MFMA phase always folds the previous tile's weights");
+        constexpr int first = 0, end = DO_QK ? NP + NQ : NP;
+        const unsigned ka = kaddr(j), va = vaddr(jp);
+        // ring slots not filled ahead of the barrier: the QK operands among the first LA
+        // when the PV product is shorter than LA
+        static_for<NPRE, LA>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (first + i < end) ring[i] = fetch(std::integral_constant<int, first + i>{}, kb_, vb_);
+            if constexpr (first + i < end) ring[i] = fetch(std::integral_constant<int, first + i>{}, ka, va);
         });
         static_for<first, end>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             constexpr int slot = (i - first) % LA;
-            const u32x4 op = ring[slot];
-            if constexpr (i + LA < end) ring[slot] = fetch(std::integral_constant<int, i + LA>{}, kb_, vb_);
-            if constexpr (i < NQ) {
-                constexpr int ds = i >> 1, kb = i & 1;
-                s[kb] = Half<T>::mfma(op, qf[ds], s[kb]);
-            } else {
-                constexpr int pi = i - NQ, t = pi / NDB, db = pi % NDB;
+            u32x4 op = ring[slot];
+            if constexpr (i + LA < end) ring[slot] = fetch(std::integral_constant<int, i + LA>{}, ka, va);
+            // operations issued after fetch i and still allowed in flight
+            constexpr int last_issued = (i + LA < end) ? i + LA : end - 1;
+            constexpr int pending = [&]() constexpr {
+                int c = 0;
+                for (int q = i + 1; q <= last_issued; ++q) c += (q < NP ? 2 : 1);
+                return c;
+            }();
+            lgkm_wait<pending>(op);
+            if constexpr (i < NP) {
+                constexpr int t = i / NDB, db = i % NDB;
                 const u32x4 pb = {pk[t >> 1][4 * (t & 1) + 0], pk[t >> 1][4 * (t & 1) + 1],
                                   pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
                 oacc[db] = Half<T>::mfma(op, pb, oacc[db]);
+                // first tree level of the previous tile's weight sum (s still holds them):
+                // pair q of the 16 is added at PV step q mod NP
+                static_for<0, 16>([&](auto qc) __attribute__((always_inline)) {
+                    constexpr int q = decltype(qc)::value;
+                    if constexpr (q % NP == i) part[q] = s[q >> 3][2 * (q & 7)] + s[q >> 3][2 * (q & 7) + 1];
+                });
+                if constexpr (i == 2 || (NP <= 2 && i == NP - 1)) issue_tiles(j + 2);
+            } else {
+                constexpr int qi = i - NP, ds = qi >> 1, kb = qi & 1;
+                // the first k-step of each key block starts from a zero accumulator
+                s[kb] = Half<T>::mfma(op, qf[ds], ds == 0 ? f32x16{} : s[kb]);
+                // remaining tree levels (8, 4, 2, 1 partial sums = reduction ops 0..14, in
+                // dependency order), spread over the NQ QK steps
+                static_for<(qi * 15) / NQ, ((qi + 1) * 15) / NQ>([&](auto rc) __attribute__((always_inline)) {
+                    constexpr int r = decltype(rc)::value;
+                    constexpr int o = r < 8 ? r : r < 12 ? r - 8 : r < 14 ? r - 12 : 0;
+                    part[o] = part[2 * o] + part[2 * o + 1];
+                });
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        if constexpr (!DO_QK) {
+#pragma unroll
+            for (int n2 = 8; n2 >= 1; n2 /= 2)
+#pragma unroll
+                for (int i = 0; i < n2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
+        }
+        l_run += part[0];
     };
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
-    auto mphase = [&](bool do_qk, int j, bool do_pv, int jp) __attribute__((always_inline)) {
-        if (do_qk && do_pv) mphase_t(yes{}, yes{}, j, jp);
-        else if (do_qk) mphase_t(yes{}, no{}, j, jp);
-        else if (do_pv) mphase_t(no{}, yes{}, j, jp);
-    };
-    auto softmax = [&](int j) __attribute__((always_inline)) {
+    float mt = 0.0f, cc = 1.0f;
+    auto tile_max = [&](int j) __attribute__((always_inline)) {
         const int k0 = j * BC;
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        l_run += softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+        mt = tile_max_log2<2, CAUSAL>(s, c, masked, k0, Nk, myq, h32, &cc);
+    };
+    auto softmax = [&]() __attribute__((always_inline)) {
+        tile_exp<2, NDB>(s, oacc, m_run, l_run, mt, cc);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
     };
 
-    // prologue: K_0 resident before the first MFMA phase
-    issue_tile(kpc{}, kg, 0, kbuf(0));
+    // prologue: K_0, V_0, K_1, V_1 resident before the first phase
+    issue_tiles(0);
+    issue_tiles(1);
     wait_loads();
     __syncthreads();
+    prefetch_pv(0);  // operands of the first (zero-weight) PV product
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.0f;  // no previous tile to fold into l
 
-    if (grp == 0) {
-        for (int j = 0; j < n; ++j) {
-            // MFMA phase (global phase 2j)
-            issue_stage(j);
-            mphase(j <= last, j, j > 0 && j - 1 <= last, j - 1);
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-            // softmax phase (global phase 2j+1)
-            if (j <= last) softmax(j);
-            wait_loads();
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-        }
-        mphase(false, n - 1, n - 1 <= last, n - 1);
-        __syncthreads();
-    } else {
-        issue_stage(0);
-        __syncthreads();
-        for (int j = 0; j < n; ++j) {
-            // MFMA phase (global phase 2j+1)
-            mphase(j <= last, j, j > 0 && j - 1 <= last, j - 1);
-            wait_loads();
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-            // softmax phase (global phase 2j+2)
-            issue_stage(j + 1);
-            if (j <= last) softmax(j);
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-        }
-        mphase(false, n - 1, n - 1 <= last, n - 1);
+    const bool g0 = grp == 0;
+    if (!g0) barrier_nofence();  // group 1 starts one phase later
+    for (int j = 0; j < n; ++j) {
+        // MFMA phase: group 0 in global phase 2j, group 1 in 2j+1
+        wait_loads();  // this wave's loads from its previous MFMA phase
+        mphase_t(yes{}, yes{}, j, j > 0 ? j - 1 : 0);
+        tile_max(j);
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_nofence();
+        // softmax phase: group 0 in global phase 2j+1, group 1 in 2j+2
+        softmax();
+        prefetch_pv(j);
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_nofence();
     }
+    mphase_t(no{}, yes{}, n - 1, n - 1);
+    if (g0) barrier_nofence();
 
     // epilogue: O = O / l, L = (m + log2 l) ln 2
     const float l_tot = wave_half_sum(l_run);
@@ -703,7 +861,8 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
         }
 
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        l_run += softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+        softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+        l_run += tile_sum<NKB>(s);
 
         // O^T += V^T P^T, one key per lane half per MFMA: k-step r of block kb is
         // key kb*32 + 8*(r/4) + 4*h32 + r%4, the key the lane's S^T register r holds.

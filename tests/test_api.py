@@ -77,11 +77,13 @@ def test_select_config(dtype, d):
     assert cfg["Bc"] in (32, 64)
     s = 4 if dtype == "f32" else 2
     if cfg["waves"] == 8:
-        # ping-pong kernel: double-buffered, swizzled K and V tiles (96-wide rows padded to 128),
-        # one workgroup per CU
+        # ping-pong kernel, one workgroup per CU
         assert dtype != "f32" and d % 8 == 0
-        pitch = 256 if cfg["dpad"] > 64 else cfg["dpad"] * s
-        lds = 4 * cfg["Bc"] * pitch
+        # three K and four V tile buffers; K rows padded to an odd chunk count, V rows to
+        # 4 or 12 chunks mod 16
+        kp = cfg["dpad"] // 8 + 1
+        vp = cfg["dpad"] // 8 + (4 if cfg["dpad"] in (64, 128) else 0)
+        lds = cfg["Bc"] * 16 * (3 * kp + 4 * vp)
         assert lds <= 160 * 1024
     else:
         # 4-wave kernel: K with a 16-byte row pad, V padded for its transposed reads
