@@ -450,21 +450,23 @@ template <int DP> struct Pitch {
 // vector ALU work at the same time. Global phase 2m is group 0's MFMA phase m and group 1's
 // softmax phase m-1; phase 2m+1 is group 1's MFMA phase m and group 0's softmax phase m.
 //  * MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T. Around the MFMAs the
-//    wave also folds the fp32 weights of tile j-1 into l, issues the direct HBM->LDS loads
-//    of K_{j+2} and V_{j+2} (its share), and after the last MFMA applies the masks and takes
-//    the row max of S_j.
-//  * Softmax phase j: the rescale test, exp2 of the tile, packing P_j to 16 bits, and the
-//    first PV operands of the next MFMA phase (read ahead of the barrier).
-// The vector work left in the softmax phase is what the PV product waits for; the rest runs
-// in the gaps of the MFMA phase. Each wave awaits its loads at the start of its next MFMA
-// phase, before the end of global phase 2j+3. K has three LDS buffers (K_j is read in MFMA
-// phase j), V four (V_j is read at the end of softmax phase j and in MFMA phase j+1), so no
-// buffer is rewritten while either group may still read it. Tail rows of K/V are clamped to
-// row Nk-1. Both groups run one loop body (their differences are scalar flags), so the
-// accumulators keep fixed registers. Every MFMA phase runs the full program: the first one
-// multiplies a zero P by the resident V_0, and a causal wave past its diagonal runs fully
-// masked tiles whose weights are exactly zero; the phases are barrier-bound, so neither
-// costs time.
+//    wave also folds the fp32 weights of tile j-1 into l, and after the last MFMA applies
+//    the masks and takes the row max of S_j.
+//  * Softmax phase j: the wave's share of the direct HBM->LDS copies of K_{j+2} and V_{j+2},
+//    the rescale test, exp2 of the tile, packing P_j to 16 bits, and the first PV operands
+//    of the next MFMA phase (read ahead of the barrier).
+// Copies are issued from the softmax phase because issuing them stalls the issuing wave for
+// a while; there the stall does not hold up the matrix core. The copies a group issues in
+// its softmax phase j are awaited in global phase 2j+3 (group 0 at the start of its
+// softmax phase j+1, group 1 at the end of its MFMA phase j+1), so they are in LDS when
+// the barrier ending that phase lets group 0 start MFMA phase j+2. K has three LDS buffers (K_j is read
+// in MFMA phase j), V four (V_j is read at the end of softmax phase j and in MFMA phase
+// j+1), so no buffer is rewritten while either group may still read it. Tail rows of K/V
+// are clamped to row Nk-1. Both groups run one loop body (their differences are scalar
+// flags), so the accumulators keep fixed registers. Every MFMA phase runs the full program:
+// the first one multiplies a zero P by the resident V_0, and a causal wave past its diagonal
+// runs fully masked tiles whose weights are exactly zero; the phases are barrier-bound, so
+// neither costs time.
 template <typename T, int DP, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
@@ -508,64 +510,49 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int n = (kv_end + BC - 1) / BC;
     const int dchunks = d / 8;
 
-    // Direct HBM->LDS load of one K or V tile into rows of PITCH chunks: wave instruction idx
-    // fills LDS chunks [64*idx, 64*idx+64) (wave-uniform destination, lane i -> +16*i); lanes
-    // on padding chunks are masked off. The lane's source offset within a full tile is fixed,
-    // so it is computed once (slot_off; -1 = padding lane). A tile that runs past Nk repeats
-    // row Nk-1 in its tail rows (finite; their scores are masked and their weights are zero).
-    constexpr int KIT = (KP + NWAVE - 1) / NWAVE, VIT = (VP + NWAVE - 1) / NWAVE;
-    int koff[KIT], voff[VIT];
-    auto init_slots = [&](auto pitch_c, int* off) __attribute__((always_inline)) {
-        constexpr int PITCH = decltype(pitch_c)::value;
+    // Direct HBM->LDS copy of the K and V tiles into rows of KP / VP chunks. The copy of a
+    // tile pair is KP + VP wave instructions (64 lanes x 16 B, wave-uniform LDS destination,
+    // lane i -> +16*i); instruction c = it*NWAVE + wave belongs to this wave. A lane on a
+    // padding chunk loads a valid chunk of its row into the padding, which is never read, so
+    // the copy of a full tile needs no lane mask. Chunks past d (DP > d) repeat the row's last
+    // data chunk: finite, and Q is zero there, so they add nothing to the scores. A tile that
+    // runs past Nk repeats row Nk-1 in its tail rows (finite; their scores are masked and
+    // their weights are zero); only that last tile takes the slower clamped path.
+    constexpr int NCP = (KP + VP + NWAVE - 1) / NWAVE;
+    unsigned coff[NCP];  // lane's byte offset within a full tile (row r, column chunk)
 #pragma unroll
-        for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
-            const int idx = it * NWAVE + wave;
-            const int p = idx * 64 + lane;
-            const int r = p / PITCH, cch = p - r * PITCH;
-            off[it] = (idx < PITCH && cch < DCH) ? (r * d + min(cch, dchunks - 1) * 8) * 2 : -1;
-        }
-    };
-    auto issue_tile = [&](auto pitch_c, const uint16_t* src, int tile, uint8_t* dst, const int* off)
-                          __attribute__((always_inline)) {
-        constexpr int PITCH = decltype(pitch_c)::value;
-        if (tile * BC + BC <= Nk) {
-            const uint8_t* base = (const uint8_t*)(src + (int64_t)tile * BC * d);
-#pragma unroll
-            for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
-                const int idx = it * NWAVE + wave;
-                if (idx < PITCH && off[it] >= 0)
-                    __builtin_amdgcn_global_load_lds((const void*)(base + off[it]),
-                                                     (FA_LDS void*)(dst + idx * 1024), 16, 0, 0);
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < (PITCH + NWAVE - 1) / NWAVE; ++it) {
-                const int idx = it * NWAVE + wave;
-                if (idx < PITCH) {
-                    const int p = idx * 64 + lane;
-                    const int r = p / PITCH, cch = p - r * PITCH;
-                    const int gr = min(tile * BC + r, Nk - 1);
-                    // chunks past d (DP > d) repeat the row's last data chunk: finite, and Q
-                    // is zero there, so they add nothing to the scores
-                    const int gc = min(cch, dchunks - 1) * 8;
-                    if (cch < DCH)
-                        __builtin_amdgcn_global_load_lds((const void*)(src + (int64_t)gr * d + gc),
-                                                         (FA_LDS void*)(dst + idx * 1024), 16, 0, 0);
-                }
-            }
-        }
-    };
+    for (int it = 0; it < NCP; ++it) {
+        const int c = it * NWAVE + wave;
+        const int pitch = c < KP ? KP : VP;
+        const int idx = c < KP ? c : c - KP;
+        const int p = idx * 64 + lane;
+        const int r = p / pitch, cch = p - r * pitch;
+        coff[it] = (unsigned)(r * d + min(cch, dchunks - 1) * 8) * 2u;
+    }
     auto kbuf = [&](int j) __attribute__((always_inline)) { return smem + (j % NKBUF) * KTILEB; };
     auto vbuf = [&](int j) __attribute__((always_inline)) { return smem + NKBUF * KTILEB + (j % NVBUF) * VTILEB; };
-    using kpc = std::integral_constant<int, KP>;
-    using vpc = std::integral_constant<int, VP>;
-    init_slots(kpc{}, koff);
-    init_slots(vpc{}, voff);
-    auto issue_tiles = [&](int m) __attribute__((always_inline)) {  // K_m and V_m
-        if (m < n) {
-            issue_tile(kpc{}, kg, m, kbuf(m), koff);
-            issue_tile(vpc{}, vg, m, vbuf(m), voff);
+    // copy instruction `it` of this wave for tile m (wave-uniform branches only)
+    auto issue_copy = [&](int it, int m) __attribute__((always_inline)) {
+        const int c = it * NWAVE + wave;
+        if (m >= n || c >= KP + VP) return;
+        const bool isk = c < KP;
+        const int idx = isk ? c : c - KP;
+        const uint8_t* tile = (const uint8_t*)((isk ? kg : vg) + (int64_t)m * BC * d);
+        uint8_t* dst = (isk ? kbuf(m) : vbuf(m)) + idx * 1024;
+        if (m * BC + BC <= Nk) {
+            __builtin_amdgcn_global_load_lds((const void*)(tile + coff[it]), (FA_LDS void*)dst, 16, 0, 0);
+        } else {
+            const int pitch = isk ? KP : VP;
+            const int p = idx * 64 + lane;
+            const int r = p / pitch, cch = p - r * pitch;
+            const int rr = min(r, Nk - 1 - m * BC);
+            const unsigned off = (unsigned)(rr * d + min(cch, dchunks - 1) * 8) * 2u;
+            __builtin_amdgcn_global_load_lds((const void*)(tile + off), (FA_LDS void*)dst, 16, 0, 0);
         }
+    };
+    auto issue_tiles = [&](int m) __attribute__((always_inline)) {  // all of K_m and V_m
+#pragma unroll
+        for (int it = 0; it < NCP; ++it) issue_copy(it, m);
     };
     auto wait_loads = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -657,7 +644,6 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
                     constexpr int q = decltype(qc)::value;
                     if constexpr (q % NP == i) part[q] = s[q >> 3][2 * (q & 7)] + s[q >> 3][2 * (q & 7) + 1];
                 });
-                if constexpr (i == 2 || (NP <= 2 && i == NP - 1)) issue_tiles(j + 2);
             } else {
                 constexpr int qi = i - NP, ds = qi >> 1, kb = qi & 1;
                 // the first k-step of each key block starts from a zero accumulator
@@ -709,12 +695,17 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     if (!g0) barrier_nofence();  // group 1 starts one phase later
     for (int j = 0; j < n; ++j) {
         // MFMA phase: group 0 in global phase 2j, group 1 in 2j+1
-        wait_loads();  // this wave's loads from its previous MFMA phase
         mphase_t(yes{}, yes{}, j, j > 0 ? j - 1 : 0);
         tile_max(j);
         __builtin_amdgcn_sched_barrier(0);
+        // this wave's copies of tile j+1 (issued in its previous softmax phase) must land
+        // before the barrier that ends global phase 2j+1: group 1 waits at the end of this
+        // MFMA phase, group 0 right after the barrier (its phase 2j+1 is the next one)
+        if (!g0) wait_loads();
         barrier_nofence();
+        if (g0) wait_loads();
         // softmax phase: group 0 in global phase 2j+1, group 1 in 2j+2
+        issue_tiles(j + 2);
         softmax();
         prefetch_pv(j);
         __builtin_amdgcn_sched_barrier(0);
