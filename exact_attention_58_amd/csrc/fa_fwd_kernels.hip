@@ -767,8 +767,11 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NKB = BC / 32;
     constexpr int NDB = DP / 32;
 
-    __shared__ __attribute__((aligned(16))) float Ks[BC * KST];
-    __shared__ __attribute__((aligned(16))) float Vs[BC * VST];
+    // Two K/V buffers when two workgroups still fit the CU's 160 KiB of LDS: tile j+1 is
+    // stored while tile j is read, one barrier per tile. Otherwise one buffer, two barriers.
+    constexpr int NBUF = 2 * 2 * BC * (KST + VST) * 4 <= 160 * 1024 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) float Ks[NBUF][BC * KST];
+    __shared__ __attribute__((aligned(16))) float Vs[NBUF][BC * VST];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
@@ -811,13 +814,13 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
             vreg[cc] = load_chunk32<VEC>(vg, j * BC + row, col, Nk, d);
         }
     };
-    auto store_tile = [&]() __attribute__((always_inline)) {
+    auto store_tile = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
             const int chunk = tid + cc * 64 * NW;
             const int row = chunk / CPR, col = (chunk % CPR) * 4;
-            *(f32x4*)(Ks + row * KST + col) = kreg[cc];
-            *(f32x4*)(Vs + row * VST + col) = vreg[cc];
+            *(f32x4*)(Ks[b] + row * KST + col) = kreg[cc];
+            *(f32x4*)(Vs[b] + row * VST + col) = vreg[cc];
         }
     };
 
@@ -827,46 +830,66 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     float m_run = kNegInf, l_run = 0.0f;
     const float c = a.scale_log2;
 
-    load_tile(0);
-    for (int j = 0; j < n_tiles; ++j) {
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (j + 1 < n_tiles) load_tile(j + 1);
-
+    // one key tile: QK^T, masks and online softmax, PV (Kb / Vb: the LDS buffer holding it)
+    auto tile = [&](int j, const float* Kb, const float* Vb) __attribute__((always_inline)) {
         const int k0 = j * BC;
-        if (CAUSAL && k0 > r0w + 31) continue;
-
-        f32x16 s[NKB];
+        // a causal wave skips tiles wholly above its rows (the workgroup still loads them
+        // for its other waves)
+        if (!CAUSAL || k0 <= r0w + 31) {
+            f32x16 s[NKB];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = f32x16{};
-            const float* kp = Ks + (kb * 32 + l32) * KST + h32 * HALF;
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[kb] = f32x16{};
+                const float* kp = Kb + (kb * 32 + l32) * KST + h32 * HALF;
 #pragma unroll
-            for (int c4 = 0; c4 < HALF / 4; ++c4) {
-                const f32x4 kv = *(const f32x4*)(kp + 4 * c4);
+                for (int c4 = 0; c4 < HALF / 4; ++c4) {
+                    const f32x4 kv = *(const f32x4*)(kp + 4 * c4);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], qf[4 * c4 + e], s[kb], 0, 0, 0);
+                    for (int e = 0; e < 4; ++e)
+                        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[e], qf[4 * c4 + e], s[kb], 0, 0, 0);
+                }
             }
+
+            const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
+            softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+            l_run += tile_sum<NKB>(s);
+
+            // O^T += V^T P^T, one key per lane half per MFMA: k-step r of block kb is
+            // key kb*32 + 8*(r/4) + 4*h32 + r%4, the key the lane's S^T register r holds.
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                    const float* vp = Vb + key * VST + l32;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vp[db * 32], s[kb][r], oacc[db], 0, 0, 0);
+                }
         }
-
-        const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
-        l_run += tile_sum<NKB>(s);
-
-        // O^T += V^T P^T, one key per lane half per MFMA: k-step r of block kb is
-        // key kb*32 + 8*(r/4) + 4*h32 + r%4, the key the lane's S^T register r holds.
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kb * 32 + 8 * (r >> 2) + 4 * h32 + (r & 3);
-                const float* vp = Vs + key * VST + l32;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vp[db * 32], s[kb][r], oacc[db], 0, 0, 0);
-            }
+    };
+    if constexpr (NBUF == 2) {
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+        if (n_tiles > 1) load_tile(1);
+        for (int j = 0; j < n_tiles; ++j) {
+            tile(j, Ks[j & 1], Vs[j & 1]);
+            // tile j+1 goes to the other buffer, whose last readers (tile j-1) passed the
+            // previous barrier; this barrier publishes it and retires buffer j & 1
+            if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+            __syncthreads();
+            if (j + 2 < n_tiles) load_tile(j + 2);
+        }
+    } else {
+        load_tile(0);
+        for (int j = 0; j < n_tiles; ++j) {
+            __syncthreads();
+            store_tile(0);
+            __syncthreads();
+            if (j + 1 < n_tiles) load_tile(j + 1);
+            tile(j, Ks[0], Vs[0]);
+        }
     }
 
     const float l_tot = wave_half_sum(l_run);

@@ -101,6 +101,13 @@ def test_select_config_grid_fill(dtype):
     assert small["waves"] == 4 and small["Br"] == 128
     odd_d = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 100, False, num_cus=256)
     assert odd_d["waves"] == 4
+    # short key sequences (HBM-bound) stay on the 4-wave kernel
+    short = fa.fa_select_config(dtype, 64, 128, 128, 128, 128, False, num_cus=256)
+    assert short["waves"] == 4
+    edge = fa.fa_select_config(dtype, 16, 128, 512, 512, 128, False, num_cus=256)
+    assert edge["waves"] == 4
+    longer = fa.fa_select_config(dtype, 8, 128, 1024, 513, 128, False, num_cus=256)
+    assert longer["waves"] == 8
 
 
 def test_select_config_errors():
