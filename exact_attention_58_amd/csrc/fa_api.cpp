@@ -53,7 +53,6 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
 
 int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
                   int num_cus, bool aligned, TileConfig* out) {
-    (void)causal;
     TileConfig c{};
     c.dpad = (int)((d + 31) / 32) * 32;
     c.waves = 4;
@@ -68,9 +67,14 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // go to the 4-wave kernel, whose smaller workgroups overlap their loads better
         // (bf16 d=128, N=128: 4.7 vs 2.8 TB/s on MI355X).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
+        const int64_t wgs128 = (Nq + 127) / 128 * B * H;
         if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > 512) {
             c.waves = 8;
             c.br = 256;
+        } else if (!causal && c.dpad <= 96 && wgs128 < num_cus && Nk > 2 * c.bc) {
+            // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
+            // block's keys walked in two halves by two waves and merged at the end
+            c.br = 64;
         }
     }
     // The grid must stay within the 32-bit launch limit.

@@ -288,12 +288,18 @@ __device__ inline u32x4 load_chunk16(const uint16_t* base, int row, int col, int
     return r;
 }
 
-// 16-bit forward kernel. DP: padded head dim (32, 64, 96, 128). Workgroup = 4 waves
-// = 128 query rows; K/V tiles of 64 keys.
-template <typename T, int DP, bool CAUSAL, bool VEC>
+// 16-bit forward kernel. DP: padded head dim (32, 64, 96, 128). Workgroup = 4 waves; K/V
+// tiles of 64 keys. SPLIT = 1: 4 row blocks of 32 = 128 query rows, every wave walks all
+// key tiles. SPLIT = 2 (non-causal grids too small to fill the chip): 2 row blocks = 64
+// rows, and the two waves of a row block each walk one half of the key tiles (two tiles
+// staged per step); at the end the second half's (O, m, l) pass through LDS and the first
+// half merges them: m = max(m1, m2), l = l1 2^(m1-m) + l2 2^(m2-m), O likewise, the same
+// exact combination the online recurrence makes tile by tile.
+template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
-    constexpr int NW = 4, BR = 32 * NW, BC = 64;
+    static_assert(SPLIT == 1 || (SPLIT == 2 && !CAUSAL), "key split: non-causal only");
+    constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB, BC = 64;
     constexpr int KST = DP + 8;   // K row stride (elements): 16-byte pad, conflict-free b128 reads
     // V row stride: 4 consecutive rows must start in 4 distinct quarters of the 16 bank groups
     // (the transposed read serves 4 rows x 4 chunks at once): 20 or 12 chunks for d 128 / 64,
@@ -305,11 +311,17 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NDS = DP / 16;  // k-steps of the QK^T product
     constexpr int NDB = DP / 32;  // 32-wide head-dim blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KST];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[BC * VST];
+    // SPLIT tile buffers; after the key loop the same memory carries the split merge
+    constexpr int TILE_ELEMS = BC * KST + BC * VST;
+    constexpr int MERGE_FLOATS = SPLIT > 1 ? RB * (NDB * 16 + 2) * 64 : 0;
+    constexpr int SMEM_B = SPLIT * TILE_ELEMS * 2 > MERGE_FLOATS * 4 ? SPLIT * TILE_ELEMS * 2 : MERGE_FLOATS * 4;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM_B];
+    auto Ksb = [&](int h) __attribute__((always_inline)) { return (uint16_t*)smem + h * TILE_ELEMS; };
+    auto Vsb = [&](int h) __attribute__((always_inline)) { return (uint16_t*)smem + h * TILE_ELEMS + BC * KST; };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
+    const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = wg / n_qtiles;
@@ -317,7 +329,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int q0 = qt * BR;
-    const int r0w = q0 + wave * 32;
+    const int r0w = q0 + rbk * 32;
     const int myq = r0w + l32;
 
     const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
@@ -332,26 +344,36 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     int kv_end = Nk;
     if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
     const int n_tiles = (kv_end + BC - 1) / BC;
+    // key half h walks tiles [h * n_steps, min(n_tiles, (h + 1) * n_steps))
+    const int n_steps = (n_tiles + SPLIT - 1) / SPLIT;
 
-    u32x4 kreg[CH], vreg[CH];
-    auto load_tile = [&](int j) __attribute__((always_inline)) {
+    // step i stages tile h * n_steps + i of every half h (rows past Nk load as zeros)
+    u32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
+    auto load_tile = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 64 * NW;
-            const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            kreg[c] = load_chunk16<VEC>(kg, j * BC + row, col, Nk, d);
-            vreg[c] = load_chunk16<VEC>(vg, j * BC + row, col, Nk, d);
-        }
+        for (int h = 0; h < SPLIT; ++h)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * 64 * NW;
+                const int row = chunk / CPR, col = (chunk % CPR) * 8;
+                const int j = h * n_steps + i;
+                kreg[h][c] = load_chunk16<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+                vreg[h][c] = load_chunk16<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+            }
     };
     auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 64 * NW;
-            const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            *(u32x4*)(Ks + row * KST + col) = kreg[c];
-            *(u32x4*)(Vs + row * VST + col) = vreg[c];
-        }
+        for (int h = 0; h < SPLIT; ++h)
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * 64 * NW;
+                const int row = chunk / CPR, col = (chunk % CPR) * 8;
+                *(u32x4*)(Ksb(h) + row * KST + col) = kreg[h][c];
+                *(u32x4*)(Vsb(h) + row * VST + col) = vreg[h][c];
+            }
     };
+    const uint16_t* Ks = Ksb(half);
+    const uint16_t* Vs = Vsb(half);
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -360,12 +382,14 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const float c = a.scale_log2;
 
     load_tile(0);
-    for (int j = 0; j < n_tiles; ++j) {
+    for (int i = 0; i < n_steps; ++i) {
         __syncthreads();
         store_tile();
         __syncthreads();
-        if (j + 1 < n_tiles) load_tile(j + 1);
+        if (i + 1 < n_steps) load_tile(i + 1);
 
+        const int j = half * n_steps + i;
+        if (SPLIT > 1 && j >= n_tiles) continue;  // the last half may have one tile less
         const int k0 = j * BC;
         if (CAUSAL && k0 > r0w + 31) continue;  // every key of the tile is above this wave's rows
 
@@ -401,6 +425,33 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
                 oacc[db] = Half<T>::mfma(va, pb, oacc[db]);
             }
         }
+    }
+
+    if constexpr (SPLIT > 1) {
+        // ---- merge the key halves: half 1 hands (O, m, l) to half 0 through LDS
+        // (lane-contiguous rows of 64 floats: conflict-free)
+        constexpr int NV = NDB * 16 + 2;
+        float* mrg = (float*)smem + rbk * NV * 64;
+        __syncthreads();  // every wave is done with the tile buffers
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mrg[(db * 16 + r) * 64 + lane] = oacc[db][r];
+            mrg[(NV - 2) * 64 + lane] = m_run;
+            mrg[(NV - 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m2 = mrg[(NV - 2) * 64 + lane], l2 = mrg[(NV - 1) * 64 + lane];
+        const float m = fmaxf(m_run, m2);  // finite: half 0 has seen key tile 0
+        const float a1 = __builtin_amdgcn_exp2f(m_run - m), a2 = __builtin_amdgcn_exp2f(m2 - m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a1 + mrg[(db * 16 + r) * 64 + lane] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_run = m;
     }
 
     // ---- epilogue: O = O / l, L = (m + log2 l) ln 2
@@ -932,11 +983,17 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
         return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
     }
     if (a.causal) {
-        return vec ? launch(fwd16_kernel<T, DP, true, true>, a, 128, st, 256)
-                   : launch(fwd16_kernel<T, DP, true, false>, a, 128, st, 256);
+        return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256)
+                   : launch(fwd16_kernel<T, DP, true, false, 1>, a, 128, st, 256);
     }
-    return vec ? launch(fwd16_kernel<T, DP, false, true>, a, 128, st, 256)
-               : launch(fwd16_kernel<T, DP, false, false>, a, 128, st, 256);
+    if constexpr (DP <= 96) {
+        if (cfg.br == 64) {  // key split in two (non-causal, small grids)
+            return vec ? launch(fwd16_kernel<T, DP, false, true, 2>, a, 64, st, 256)
+                       : launch(fwd16_kernel<T, DP, false, false, 2>, a, 64, st, 256);
+        }
+    }
+    return vec ? launch(fwd16_kernel<T, DP, false, true, 1>, a, 128, st, 256)
+               : launch(fwd16_kernel<T, DP, false, false, 1>, a, 128, st, 256);
 }
 
 template <int DP, int BC>

@@ -73,7 +73,7 @@ def test_unsupported(L, kw):
 def test_select_config(dtype, d):
     cfg = fa.fa_select_config(dtype, 4, 16, 4096, 4096, d, False)
     assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
-    assert cfg["Br"] == 32 * cfg["waves"]
+    assert cfg["Br"] == 32 * cfg["waves"] or (cfg["waves"] == 4 and cfg["Br"] == 64)
     assert cfg["Bc"] in (32, 64)
     s = 4 if dtype == "f32" else 2
     if cfg["waves"] == 8:
@@ -89,6 +89,8 @@ def test_select_config(dtype, d):
         # 4-wave kernel: K with a 16-byte row pad, V padded for its transposed reads
         vpad = 64 if (dtype != "f32" and cfg["dpad"] in (64, 128)) else 0
         lds = cfg["Bc"] * (cfg["dpad"] * s + 16) + cfg["Bc"] * (cfg["dpad"] * s + vpad)
+        if cfg["Br"] == 64:
+            lds *= 2  # key split: one tile buffer per key half
         assert lds * 2 <= 160 * 1024  # two workgroups per CU fit the 160 KiB LDS
 
 
@@ -98,7 +100,15 @@ def test_select_config_grid_fill(dtype):
     big = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 128, False, num_cus=256)
     assert big["waves"] == 8 and big["Br"] == 256
     small = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, False, num_cus=256)
-    assert small["waves"] == 4 and small["Br"] == 128
+    # too few 128-row workgroups: 64 rows per workgroup, keys split between two waves
+    assert small["waves"] == 4 and small["Br"] == 64
+    small_causal = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, True, num_cus=256)
+    assert small_causal["waves"] == 4 and small_causal["Br"] == 128
+    small_d128 = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 128, False, num_cus=256)
+    assert small_d128["Br"] == 128
+    # enough 128-row workgroups (d % 8 != 0 keeps the 256-row kernel out): no key split
+    filled = fa.fa_select_config(dtype, 4, 16, 1000, 3001, 90, False, num_cus=256)
+    assert filled["Br"] == 128
     odd_d = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 100, False, num_cus=256)
     assert odd_d["waves"] == 4
     # short key sequences (HBM-bound) stay on the 4-wave kernel
