@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the exact attention forward (ctypes wrapper over attn_oracle.c).
+"""fp64 CPU oracle for exact attention: the forward (ctypes wrapper over attn_oracle.c) and
+its gradients (attention_bwd, numpy on full matrices).
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does, and this
@@ -98,3 +99,53 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, threads: int |
     if rc != 0:
         raise RuntimeError(f"attn_oracle_fwd failed with status {rc}")
     return o, lse
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool):
+    """Exact gradients of the attention forward in fp64 (numpy, whole score matrix per head).
+
+    For O = softmax(S) V with S = scale * Q K^T (top-left causal mask: key j visible to query
+    i iff j <= i) and an upstream gradient dO, the chain rule gives, per (b, h):
+
+        P  = softmax(S) row by row            (exp(S - rowmax) / rowsum)
+        dV = P^T dO
+        dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))        (the softmax Jacobian applied row by row)
+        dQ = scale * dS K
+        dK = scale * dS^T Q
+
+    These are the gradients the backward kernel of page "flash_attention_2.cu" accumulates
+    (its dV, dP, dS = P (dP - D), dQ and dK updates); here they are written out on full
+    matrices with no tiling, no recomputation from L and no online recurrence. rowsum(P dP)
+    equals rowsum(dO * O) exactly in real arithmetic.
+
+    q: [B,H,Nq,d], k, v: [B,H,Nk,d], do: [B,H,Nq,d]. Returns dq, dk, dv (fp64).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    if q.ndim != 4 or k.shape[:2] != q.shape[:2] or v.shape != k.shape or do.shape != q.shape \
+            or k.shape[3] != q.shape[3]:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape} do{do.shape}")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    visible = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        visible = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None]
+    for b in range(B):
+        for h in range(H):
+            s = scale * (q[b, h] @ k[b, h].T)
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            dv[b, h] = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, h].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, h] = scale * (ds @ k[b, h])
+            dk[b, h] = scale * (ds.T @ q[b, h])
+    return dq, dk, dv
