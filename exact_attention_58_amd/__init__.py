@@ -1,6 +1,6 @@
-"""Python binding of the MI355X exact attention forward library (libfa_mi355x.so).
+"""Python binding of the MI355X exact attention library (libfa_mi355x.so).
 
-Argument marshalling only: every step of the forward pass runs in the HIP kernels
+Argument marshalling only: every step of the forward and backward passes runs in the HIP kernels
 behind the C ABI declared in include/fa.h. PyTorch is used for device memory and
 streams. There is no fallback: if the library is missing, the calls raise.
 
@@ -8,6 +8,8 @@ streams. There is no fallback: if the library is missing, the calls raise.
     fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict
     fa_status_str(code) -> str
     attention(q, k, v, scale=None, causal=False) -> (o, lse)  # allocates o and lse
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale, causal, stream=None)
+    attention_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
-EXPORTED = ("fa_fwd", "fa_status_str", "fa_select_config", "fa_version")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
 DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
 
 _lock = threading.Lock()
@@ -59,6 +61,9 @@ def lib():
             L.fa_fwd.restype = ctypes.c_int
             L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                  ctypes.c_int, ctypes.c_int, vp]
+            L.fa_bwd.restype = ctypes.c_int
+            L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                 ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
             L.fa_status_str.restype = ctypes.c_char_p
             L.fa_status_str.argtypes = [ctypes.c_int]
             ip = ctypes.POINTER(ctypes.c_int)
@@ -137,3 +142,55 @@ def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale, causal, stream)
     return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale: float, causal: bool, stream=None) -> None:
+    """Calls the C-ABI fa_bwd on contiguous device tensors (gradients and the fp32 [B,H,Nq]
+    workspace `delta` preallocated)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do),
+                    ("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for name, t, shape in (("o", o, (B, H, Nq, d)), ("do", do, (B, H, Nq, d)), ("dq", dq, (B, H, Nq, d)),
+                           ("dk", dk, (B, H, Nk, d)), ("dv", dv, (B, H, Nk, d)),
+                           ("lse", lse, (B, H, Nq)), ("delta", delta, (B, H, Nq))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+    if not all(t.dtype == q.dtype for t in (k, v, o, do, dq, dk, dv)):
+        raise TypeError("q, k, v, o, do, dq, dk, dv must share one dtype")
+    if lse.dtype != torch.float32 or delta.dtype != torch.float32:
+        raise TypeError("lse and delta must be float32")
+    dev = q.device
+    if any(t.device != dev for t in (k, v, o, lse, do, dq, dk, dv, delta)):
+        raise ValueError("all tensors must be on one device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(dev):
+        rc = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                          do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                          B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q), handle)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd")
+
+
+def attention_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, stream=None):
+    """Allocates dq, dk, dv and the workspace (torch.empty) and runs fa_bwd; returns (dq, dk, dv)."""
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale, causal, stream)
+    return dq, dk, dv

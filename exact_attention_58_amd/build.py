@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa_mi355x.so")
-SOURCES = [os.path.join(CSRC, "fa_fwd_kernels.hip"), os.path.join(CSRC, "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_fwd_kernels.hip"), os.path.join(CSRC, "fa_bwd_kernels.hip"),
+           os.path.join(CSRC, "fa_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -150,4 +150,41 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return fa::launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                 int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
+                 void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_EINVAL;
+    if (!std::isfinite(scale)) return FA_EINVAL;
+    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    const uintptr_t all16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+                            (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+    if (all16 % 2 != 0 || (uintptr_t)lse % 4 != 0 || (uintptr_t)delta % 4 != 0) return FA_EINVAL;
+    // the backward kernels exist for the 16-bit types on 16-byte rows only
+    if (dtype == FA_F32 || d % 8 != 0 || all16 % 16 != 0) return FA_EUNSUPPORTED;
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.B = (int)B;
+    a.H = (int)H;
+    a.Nq = (int)Nq;
+    a.Nk = (int)Nk;
+    a.d = (int)d;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.causal = causal ? 1 : 0;
+    a.dtype = (int)dtype;
+    const int dpad = (int)((d + 31) / 32) * 32;
+    return fa::launch_bwd(a, dpad, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
 }  // extern "C"

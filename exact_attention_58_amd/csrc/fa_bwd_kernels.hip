@@ -1,0 +1,389 @@
+// fa_bwd_kernels.hip -- exact attention backward kernels for gfx950 (MI355X, CDNA4).
+//
+// The gradients (page "flash_attention_2.cu", backward kernel): with D_i = rowsum(dO_i * O_i)
+// and P_ij = exp(scale * q_i . k_j - L_i) recomputed from the forward's logsumexp L,
+//     dV_j += P_ij dO_i,   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i),
+//     dQ_i += scale dS_ij k_j,   dK_j += scale dS_ij q_i.
+// That page accumulates dQ with atomic adds from a loop over key tiles; here three kernels
+// share the work without atomics:
+//  * row terms: D = rowsum(dO * O) per query row (fp32, into a caller's workspace);
+//  * dK, dV: one workgroup per 128 keys (4 waves x 32), looping over query tiles of 64;
+//  * dQ: one workgroup per 128 queries (4 waves x 32), looping over key tiles of 64.
+// Both tile kernels recompute S and dP on MFMA 32x32x16 (16-bit operands, fp32 accumulate);
+// P and dS are rounded to the input type for the products that consume them.
+//
+// Layouts, per wave (lane = 32 * h32 + l32):
+//  * dK/dV kernel: S = Q K^T and dP = dO V^T with this wave's keys as the MFMA columns, so a
+//    lane holds one key and 16 queries per 32-query block; the accumulator is, register for
+//    register, the A operand of dV += P^T dO and dK += dS^T Q once the queries of the
+//    reduction are enumerated in the accumulator's order; dO^T and Q^T come from LDS through
+//    ds_read_b64_tr_b16. dK and dV accumulate as [key][head-dim] blocks.
+//  * dQ kernel: S^T = K Q^T and dP^T = V dO^T with this wave's queries as the columns (the
+//    forward's layout), so dS^T is the B operand of dQ^T += K^T dS^T.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634074f;
+
+// Row terms: delta[r] = sum_c dO[r][c] O[r][c] for every flat query row r (d % 8 == 0).
+template <typename T>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, float* delta, int64_t rows, int d) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const uint16_t* op = o + r * d;
+    const uint16_t* gp = dout + r * d;
+    float acc = 0.0f;
+    for (int c = 0; c < d; c += 8) {
+        const u32x4 a = *(const u32x4*)(op + c);
+        const u32x4 b = *(const u32x4*)(gp + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a0 = Half<T>::lo(a[i]), a1 = Half<T>::hi(a[i]);
+            const float b0 = Half<T>::lo(b[i]), b1 = Half<T>::hi(b[i]);
+            acc = __builtin_fmaf(a0, b0, acc);
+            acc = __builtin_fmaf(a1, b1, acc);
+        }
+    }
+    delta[r] = acc;
+}
+
+// Tile of 64 rows x DP columns (16-bit) staged through registers into LDS rows of STR
+// elements; rows >= nrows and columns >= d are zero.
+template <int DP, int STR>
+struct TileCopy {
+    static constexpr int CPR = DP / 8;                // 16-byte chunks per row
+    static constexpr int CH = 64 * CPR / 256;         // chunks per thread
+    static_assert(64 * CPR % 256 == 0, "tile split");
+    u32x4 r[CH];
+    __device__ __attribute__((always_inline)) void load(const uint16_t* base, int row0, int nrows, int d, int tid) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int chunk = tid + c * 256;
+            const int row = chunk / CPR, col = (chunk % CPR) * 8;
+            r[c] = load_chunk16<true>(base, row0 + row, col, nrows, d);
+        }
+    }
+    __device__ __attribute__((always_inline)) void store(uint16_t* lds, int tid) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int chunk = tid + c * 256;
+            const int row = chunk / CPR, col = (chunk % CPR) * 8;
+            *(u32x4*)(lds + row * STR + col) = r[c];
+        }
+    }
+};
+
+// Transposed fragment of a 64-row LDS tile (rows = reduction index): lane gets rows
+// R + 4 h32 + {0..3} and R + 8 + 4 h32 + {0..3} of column C + 16 g16 + i16, the B (or A)
+// operand of a 32x32x16 product whose reduction runs over 16 rows in accumulator order.
+template <int STR>
+__device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* tile, int R, int C, int lane) {
+    const int h32 = lane >> 5, i16 = lane & 15, g16 = (lane >> 4) & 1;
+    const uint16_t* p = tile + (R + 4 * h32 + (i16 >> 2)) * STR + C + 16 * g16 + 4 * (i16 & 3);
+    const u32x2 lo = lds_read_tr16(p);
+    const u32x2 hi = lds_read_tr16(p + 8 * STR);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <typename T, int DP, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+    constexpr int BK = 128, BQ = 64;  // keys per workgroup, queries per tile
+    constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
+    constexpr int NDS = DP / 16, NDB = DP / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t Gs[BQ * STR];  // dO
+    __shared__ __attribute__((aligned(16))) float Ls[BQ];
+    __shared__ __attribute__((aligned(16))) float Ds[BQ];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / n_ktiles;
+    const int kt = wg - bh * n_ktiles;
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * wave;
+    const int mykey = kw0 + l32;
+
+    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
+    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
+    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+    const uint16_t* gg = (const uint16_t*)a.dout + (int64_t)bh * Nq * d;
+    const float* lg = a.lse + (int64_t)bh * Nq;
+    const float* dg = a.delta + (int64_t)bh * Nq;
+
+    // this wave's keys as B operands: lane holds K[mykey][16 ds + 8 h32 + 0..7] (V likewise)
+    u32x4 kf[NDS], vf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        kf[ds] = load_chunk16<true>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
+        vf[ds] = load_chunk16<true>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
+    }
+
+    f32x16 dva[NDB], dka[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dva[i] = dka[i] = f32x16{};
+    const float c = a.scale_log2;
+
+    // query tiles that see any key of this workgroup (causal: queries >= k0)
+    const int qt0 = CAUSAL ? k0 / BQ : 0;
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    TileCopy<DP, STR> qc, gc;
+    float lrow = 0.0f, drow = 0.0f;
+    auto load_tile = [&](int qt) __attribute__((always_inline)) {
+        qc.load(qg, qt * BQ, Nq, d, tid);
+        gc.load(gg, qt * BQ, Nq, d, tid);
+        if (tid < BQ) {
+            const int q = qt * BQ + tid;
+            lrow = q < Nq ? lg[q] * kLog2e : 0.0f;
+            drow = q < Nq ? dg[q] : 0.0f;
+        }
+    };
+    if (qt0 < n_qt) load_tile(qt0);
+    for (int qt = qt0; qt < n_qt; ++qt) {
+        __syncthreads();
+        qc.store(Qs, tid);
+        gc.store(Gs, tid);
+        if (tid < BQ) {
+            Ls[tid] = lrow;
+            Ds[tid] = drow;
+        }
+        __syncthreads();
+        if (qt + 1 < n_qt) load_tile(qt + 1);
+        const int q0 = qt * BQ;
+        // a causal wave skips tiles whose queries all precede its keys
+        if (CAUSAL && q0 + BQ - 1 < kw0) continue;
+
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const uint16_t* qp = Qs + (qb * 32 + l32) * STR + 8 * h32;
+            const uint16_t* gp = Gs + (qb * 32 + l32) * STR + 8 * h32;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                s = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], s);
+                dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+            }
+            // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey
+            unsigned ppk[8], spk[8];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ql = qb * 32 + 8 * g + 4 * h32;
+                const f32x4 lv = *(const f32x4*)(Ls + ql);
+                const f32x4 dv = *(const f32x4*)(Ds + ql);
+                float pv[4], sv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q = q0 + ql + e;
+                    const bool ok = mykey < Nk && q < Nq && (!CAUSAL || mykey <= q);
+                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
+                    pv[e] = p;
+                    sv[e] = p * (dp[4 * g + e] - dv[e]);
+                }
+                ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
+                spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
+            }
+            // dV += P^T dO and dK += dS^T Q over the two 16-query steps of this block
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 pa = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
+                const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
+                    const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
+                    dva[db] = Half<T>::mfma(pa, gb, dva[db]);
+                    dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
+                }
+            }
+        }
+    }
+
+    // register r of block db: key kw0 + 8 (r/4) + 4 h32 + r%4, column db*32 + l32
+    uint16_t* dkg = (uint16_t*)a.dk + (int64_t)bh * Nk * d;
+    uint16_t* dvg = (uint16_t*)a.dv + (int64_t)bh * Nk * d;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int col = db * 32 + l32;
+        if (col >= d) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            if (key < Nk) {
+                dvg[(int64_t)key * d + col] = Half<T>::one(dva[db][r]);
+                dkg[(int64_t)key * d + col] = Half<T>::one(dka[db][r] * sc);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <typename T, int DP, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
+    constexpr int BR = 128, BC = 64;  // queries per workgroup, keys per tile
+    constexpr int STR = DP + 8;
+    constexpr int NDS = DP / 16, NDB = DP / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[BC * STR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / n_qtiles;
+    int qt = wg - bh * n_qtiles;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int q0 = qt * BR;
+    const int r0w = q0 + 32 * wave;
+    const int myq = r0w + l32;
+
+    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
+    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
+    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+    const uint16_t* gg = (const uint16_t*)a.dout + (int64_t)bh * Nq * d;
+
+    // this wave's queries as B operands: lane holds Q[myq][16 ds + 8 h32 + 0..7] (dO likewise)
+    u32x4 qf[NDS], gf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+        qf[ds] = load_chunk16<true>(qg, myq, ds * 16 + 8 * h32, Nq, d);
+        gf[ds] = load_chunk16<true>(gg, myq, ds * 16 + 8 * h32, Nq, d);
+    }
+    const float lq = myq < Nq ? a.lse[(int64_t)bh * Nq + myq] * kLog2e : 0.0f;
+    const float dq = myq < Nq ? a.delta[(int64_t)bh * Nq + myq] : 0.0f;
+    const float c = a.scale_log2;
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    f32x16 dqa[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
+
+    TileCopy<DP, STR> kc, vc;
+    kc.load(kg, 0, Nk, d, tid);
+    vc.load(vg, 0, Nk, d, tid);
+    for (int j = 0; j < n_tiles; ++j) {
+        __syncthreads();
+        kc.store(Ks, tid);
+        vc.store(Vs, tid);
+        __syncthreads();
+        if (j + 1 < n_tiles) {
+            kc.load(kg, (j + 1) * BC, Nk, d, tid);
+            vc.load(vg, (j + 1) * BC, Nk, d, tid);
+        }
+        const int k0 = j * BC;
+        if (CAUSAL && k0 > r0w + 31) continue;
+
+        // S^T = K Q^T and dP^T = V dO^T: two 32-key blocks; register r of block kb is key
+        // k0 + kb*32 + 8 (r/4) + 4 h32 + r%4, query myq
+        unsigned pk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const uint16_t* kp = Ks + (kb * 32 + l32) * STR + 8 * h32;
+            const uint16_t* vp = Vs + (kb * 32 + l32) * STR + 8 * h32;
+#pragma unroll
+            for (int ds = 0; ds < NDS; ++ds) {
+                s = Half<T>::mfma(*(const u32x4*)(kp + ds * 16), qf[ds], s);
+                dp = Half<T>::mfma(*(const u32x4*)(vp + ds * 16), gf[ds], dp);
+            }
+            const int lim = (CAUSAL ? min(Nk - 1, myq) : Nk - 1) - k0 - kb * 32 - 4 * h32;
+            float sv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = 8 * (r >> 2) + (r & 3);
+                const float p = off <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq)) : 0.0f;
+                sv[r] = p * (dp[r] - dq);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(sv[r], sv[r + 1]);
+        }
+        // dQ^T += K^T dS^T: four 16-key steps
+#pragma unroll
+        for (int t = 0; t < BC / 16; ++t) {
+            const u32x4 sb = {pk[t >> 1][4 * (t & 1) + 0], pk[t >> 1][4 * (t & 1) + 1],
+                              pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const u32x4 ka = tr_frag<STR>(Ks, 16 * t, db * 32, lane);
+                dqa[db] = Half<T>::mfma(ka, sb, dqa[db]);
+            }
+        }
+    }
+
+    // register r of block db: column db*32 + 8 (r/4) + 4 h32 + r%4, query myq
+    if (myq < Nq) {
+        uint16_t* og = (uint16_t*)a.dq + ((int64_t)bh * Nq + myq) * d;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * h32;
+                if (d0 < d) {
+                    u32x2 w = {Half<T>::pack2(dqa[db][4 * g + 0] * sc, dqa[db][4 * g + 1] * sc),
+                               Half<T>::pack2(dqa[db][4 * g + 2] * sc, dqa[db][4 * g + 3] * sc)};
+                    *(u32x2*)(og + d0) = w;
+                }
+            }
+    }
+}
+
+template <typename T, int DP>
+int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+    hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, a.d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int n_kt = (a.Nk + 127) / 128;
+    const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
+    if (a.causal)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true>), dim3(g1), dim3(256), 0, st, a, n_kt);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false>), dim3(g1), dim3(256), 0, st, a, n_kt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int n_qt = (a.Nq + 127) / 128;
+    const unsigned g2 = (unsigned)((int64_t)n_qt * a.B * a.H);
+    if (a.causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, true>), dim3(g2), dim3(256), 0, st, a, n_qt);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, false>), dim3(g2), dim3(256), 0, st, a, n_qt);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_bwd(const BwdArgs& a, int dpad, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const bool bf = a.dtype == 2;
+    switch (dpad) {
+        case 32: return bf ? launch_bwd_t<__bf16, 32>(a, st) : launch_bwd_t<_Float16, 32>(a, st);
+        case 64: return bf ? launch_bwd_t<__bf16, 64>(a, st) : launch_bwd_t<_Float16, 64>(a, st);
+        case 96: return bf ? launch_bwd_t<__bf16, 96>(a, st) : launch_bwd_t<_Float16, 96>(a, st);
+        case 128: return bf ? launch_bwd_t<__bf16, 128>(a, st) : launch_bwd_t<_Float16, 128>(a, st);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

@@ -33,59 +33,16 @@
 
 #include <type_traits>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-#define FA_LDS __attribute__((address_space(3)))
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.693147180559945309417f;
 // Running-max refresh threshold in log2 units: O and l are rescaled only when a
 // row's max grows by more than this, otherwise the old max stays the reference.
 // The result is unchanged (numerator and denominator share the reference) and
 // the unnormalised weights stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
-
-// Workgroups are dispatched round-robin over the 8 XCDs. Renumber them so that
-// consecutive logical tiles (the query tiles of one head) run on the same XCD and
-// share its L2 for K and V.
-__device__ inline int xcd_remap(int bid, int total) {
-    constexpr int kXcds = 8;
-    const int per = total / kXcds, rem = total % kXcds;
-    const int x = bid % kXcds, slot = bid / kXcds;
-    return x * per + (x < rem ? x : rem) + slot;
-}
-
-__device__ inline float wave_half_max(float x) {
-    u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ inline float wave_half_min(float x) {
-    u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
-}
-__device__ inline float wave_half_sum(float x) {
-    u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E), fully unrolled.
-template <int B, int E, typename F>
-__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 
 // Maximum of the NKB*16 values of s as a balanced tree (v_max3), so the dependency chain is
 // logarithmic in the number of values instead of linear. MIN selects the minimum instead.
@@ -188,34 +145,6 @@ __device__ __attribute__((always_inline)) inline float tile_sum(const f32x16 (&s
     return v[0];
 }
 
-// ---------------------------------------------------------------- 16-bit types
-
-template <typename T> struct Half;
-template <> struct Half<__bf16> {
-    static __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    static __device__ inline unsigned pack2(float a, float b) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 v = {(__bf16)a, (__bf16)b};
-        return __builtin_bit_cast(unsigned, v);
-    }
-    static __device__ inline uint16_t one(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
-};
-template <> struct Half<_Float16> {
-    static __device__ inline f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    static __device__ inline unsigned pack2(float a, float b) {
-        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-        f16x2 v = {(_Float16)a, (_Float16)b};
-        return __builtin_bit_cast(unsigned, v);
-    }
-    static __device__ inline uint16_t one(float a) { return __builtin_bit_cast(uint16_t, (_Float16)a); }
-};
-
 // Packs the tile's weights to the 16-bit type (pk[kb][r/2] holds keys r, r+1 of block kb) and
 // returns the sum of the fp32 weights (a balanced tree). l sums the fp32 weights, not the
 // rounded ones: a 16-bit weight carries up to 2^-8 relative rounding error, which a row with
@@ -228,64 +157,6 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 #pragma unroll
         for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
     return sum;
-}
-
-__device__ inline u32x2 lds_read_tr16(const uint16_t* p) {
-    i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(p));
-    return __builtin_bit_cast(u32x2, t);
-}
-
-// LDS reads issued through inline asm, for kernels that also fill LDS with direct HBM->LDS
-// loads: the compiler cannot prove that a read does not alias an in-flight load and would
-// otherwise wait for every outstanding load before each LDS read. The kernel's own barrier
-// schedule guarantees that the buffers read are not being written, and the reads' completion
-// is awaited explicitly (lgkm_wait) with a count known at compile time.
-template <int OFF>
-__device__ inline u32x4 lds_rd128(unsigned addr) {
-    u32x4 r;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-    return r;
-}
-template <int OFF>
-__device__ inline u32x2 lds_rdtr16(unsigned addr) {
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-    return r;
-}
-// Waits until at most N LDS/scalar-memory operations are outstanding; tied to `x` so that
-// the consumer of x cannot be scheduled above the wait.
-template <int N>
-__device__ inline void lgkm_wait(u32x4& x) {
-    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
-}
-// Workgroup barrier without the memory fence __syncthreads() adds: that fence waits for every
-// outstanding HBM->LDS load of the issuing wave. Kernels using it order LDS traffic
-// themselves: loads are awaited with an explicit s_waitcnt vmcnt(0) one phase later, and LDS
-// reads are awaited before their results are used.
-__device__ inline void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
-__device__ inline unsigned lds_addr(const void* p) {
-    return (unsigned)(uintptr_t)(const FA_LDS void*)(p);
-}
-
-// One 16-byte chunk (8 elements) of row `row`, columns [col, col+8), zero outside
-// [0, nrows) x [0, ncols). VEC: rows are 16-byte aligned and ncols % 8 == 0.
-template <bool VEC>
-__device__ inline u32x4 load_chunk16(const uint16_t* base, int row, int col, int nrows, int ncols) {
-    u32x4 r = {0u, 0u, 0u, 0u};
-    if (row >= nrows) return r;
-    const uint16_t* p = base + (int64_t)row * ncols + col;
-    if (VEC) {
-        if (col < ncols) r = *(const u32x4*)p;
-    } else {
-        uint16_t e[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e[i] = (col + i < ncols) ? p[i] : (uint16_t)0;
-        r[0] = e[0] | ((unsigned)e[1] << 16);
-        r[1] = e[2] | ((unsigned)e[3] << 16);
-        r[2] = e[4] | ((unsigned)e[5] << 16);
-        r[3] = e[6] | ((unsigned)e[7] << 16);
-    }
-    return r;
 }
 
 // 16-bit forward kernel. DP: padded head dim (32, 64, 96, 128). Workgroup = 4 waves; K/V

@@ -1,5 +1,5 @@
 // fa_internal.h -- interface between the C-ABI front end (fa_api.cpp) and the
-// HIP kernels (fa_fwd_kernels.hip). Not installed, not part of the ABI.
+// HIP kernels (fa_fwd_kernels.hip, fa_bwd_kernels.hip). Not installed, not part of the ABI.
 #pragma once
 
 #include <stdint.h>
@@ -34,5 +34,29 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
 
 // Launches the kernel for `cfg` on `stream`; returns the hipError_t of the launch as int.
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream);
+
+// Everything the backward kernels need, already validated by the front end (16-bit types,
+// d % 8 == 0, 16-byte aligned buffers).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;      // [B,H,Nq] workspace: rowsum(dO * O)
+    int B, H, Nq, Nk, d;
+    float scale;       // softmax scale
+    float scale_log2;  // scale times log2(e)
+    int causal;
+    int dtype;
+};
+
+// Launches the three backward kernels (row terms, dK/dV, dQ) on `stream`; returns the
+// hipError_t of the launches as int.
+int launch_bwd(const BwdArgs& a, int dpad, void* stream);
 
 }  // namespace fa

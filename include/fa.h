@@ -85,6 +85,38 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                  float scale, int causal, fa_dtype dtype, void* stream);
 
+/*
+ * fa_bwd -- gradients of the attention forward, asynchronous on `stream`.
+ *
+ * Given the forward's inputs q, k, v, its outputs o and lse (as fa_fwd wrote them, same
+ * scale and causal flag) and the upstream gradient dout = dL/dO, writes
+ *     dq = dL/dQ, dk = dL/dK, dv = dL/dV
+ * by the updates of the backward kernel on page "flash_attention_2.cu" (backward kernel:
+ * D_i = rowsum(dO_i * O_i), P = exp(scale QK^T - L), dV += P^T dO, dP = dO V^T,
+ * dS = P (dP - D), dQ += scale dS K, dK += scale dS^T Q), without its atomic adds.
+ *
+ * Arguments
+ *   q, dout, dq     [B, H, Nq, d] device buffers, row-major, element type `dtype`
+ *   k, v, dk, dv    [B, H, Nk, d] device buffers, row-major, element type `dtype`
+ *   o               [B, H, Nq, d] the forward output, element type `dtype`
+ *   lse             [B, H, Nq] fp32, the forward's natural-log logsumexp
+ *   delta           [B, H, Nq] fp32 device workspace the call overwrites (rowsum(dO * O))
+ *   B, H, Nq, Nk, d, scale, causal, dtype, stream   as for fa_fwd
+ *
+ * dq, dk, dv are written in full (fp32 accumulation, rounded to nearest even); keys that no
+ * query sees (causal with Nk > Nq) get zero gradients. The caller allocates every buffer,
+ * including the workspace; the library allocates nothing. dq, dk, dv and delta must not
+ * alias each other or any input.
+ *
+ * Errors: as fa_fwd (checked before any HIP call). FA_EUNSUPPORTED also for fp32 inputs,
+ * for d not a multiple of 8 and for 16-bit buffers that are not 16-byte aligned: the
+ * backward kernels exist for bf16/fp16 rows of whole 16-byte chunks only.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, float* delta,
+                 int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                 float scale, int causal, fa_dtype dtype, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
 

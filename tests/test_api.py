@@ -28,7 +28,7 @@ def header_functions():
 
 def test_header_symbols_are_exported(L):
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_status_str", "fa_select_config", "fa_version"}
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
     assert set(fa.EXPORTED) == set(names)
@@ -66,6 +66,31 @@ def test_invalid_arguments(L, kw):
 @pytest.mark.parametrize("kw", [dict(d=129), dict(d=256), dict(Nq=2**26, d=64), dict(Nk=2**25, d=128)])
 def test_unsupported(L, kw):
     assert call(L, **kw) == fa.FA_EUNSUPPORTED
+
+
+def call_bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, delta=P, B=1, H=1, Nq=8, Nk=8, d=64,
+             scale=0.125, causal=0, dtype=2):
+    return L.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, B, H, Nq, Nk, d, ctypes.c_float(scale),
+                    causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None), dict(do=None),
+    dict(dq=None), dict(dk=None), dict(dv=None), dict(delta=None),
+    dict(B=0), dict(Nq=0), dict(Nk=0), dict(d=0), dict(dtype=3),
+    dict(scale=float("nan")), dict(B=2**40, H=2**40),
+    dict(do=P + 1), dict(dv=P + 1), dict(lse=P + 2), dict(delta=P + 2),
+])
+def test_bwd_invalid_arguments(L, kw):
+    assert call_bwd(L, **kw) == fa.FA_EINVAL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=129), dict(dtype=0), dict(d=60), dict(d=5), dict(q=P + 2), dict(dk=P + 8),
+])
+def test_bwd_unsupported(L, kw):
+    """fp32, d not a multiple of 8 and 16-bit rows off 16-byte alignment have no backward kernel."""
+    assert call_bwd(L, **kw) == fa.FA_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
