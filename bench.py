@@ -83,6 +83,33 @@ def time_workload(fa, torch, w, steps, warmup, inputs=None):
     return wall_ms, ev_ms
 
 
+def time_backward(fa, torch, w, steps, warmup):
+    """Times fa_bwd (row terms, dK/dV, dQ kernels) on the workload's inputs and a seeded
+    upstream gradient, after one forward for O and L; returns ms per call (HIP events on
+    the launch stream)."""
+    from exact_attention_58_amd.workloads import make_inputs, make_random
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in make_inputs(w))
+    do = make_random(tuple(q.shape), w.dtype, w.seed + 100).to(dev)
+    o, lse = fa.attention(q, k, v, scale=w.softmax_scale, causal=w.causal)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.softmax_scale, w.causal, stream)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.softmax_scale, w.causal, stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    del q, k, v, do, o, lse, dq, dk, dv, delta
+    return ms
+
+
 def roofline_for(w, ev_ms, sha):
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -231,6 +258,19 @@ def main():
                          "dtype": ow.dtype, "causal": ow.causal, "ms_per_step": round(wm, 4),
                          "tflops": round(ow.flops / (wm * 1e-3) / 1e12, 2), "roofline": r})
             log(f"  {name}: {wm:.3f} ms/step, {r['achieved']} TFLOP/s kernel, {100 * r['frac']:.1f}% of {ow.dtype} peak")
+        # backward (FLOP convention: 2.5 x the forward's, i.e. five products of the forward's
+        # size; this implementation recomputes S and dP in both tile kernels)
+        for name in ("d128_bf16", "d128_bf16_causal", "long_causal_bf16"):
+            ow = WORKLOADS[name]
+            ms = time_backward(fa, torch, ow, max(5, min(args.steps, 20)), 2)
+            tf = 2.5 * ow.flops / (ms * 1e-3) / 1e12
+            peak = PEAK_TFLOPS[ow.dtype]
+            also.append({"workload": f"{name} backward", "B": ow.B, "H": ow.H, "Nq": ow.Nq, "Nk": ow.Nk,
+                         "d": ow.d, "dtype": ow.dtype, "causal": ow.causal, "ms_per_step": round(ms, 4),
+                         "tflops": round(tf, 2),
+                         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                                      "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None}})
+            log(f"  {name} backward: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of {ow.dtype} peak)")
         sweep, copy_gbs = hbm_sweep(fa, torch, args.steps)
         for s in sweep:
             log(f"  short N={s['N']}: {s['GB_per_s']} GB/s ({100 * s['hbm_frac']:.1f}% of 8 TB/s)")
