@@ -275,10 +275,14 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
         }
 
         // ---- online softmax, then pack P to the 16-bit type
+        // softmax at normal priority, MFMA stretches raised: on a SIMD shared by two
+        // workgroups the products of one take precedence and the other's softmax fills in
+        __builtin_amdgcn_s_setprio(0);
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
         softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
         unsigned pk[2][8];
         l_run += pack_and_sum<T>(s, pk);
+        __builtin_amdgcn_s_setprio(1);
 
         // ---- O^T += V^T P^T: 4 k-steps of 16 keys
         const int i16 = lane & 15, g16 = (lane >> 4) & 1;
@@ -772,9 +776,14 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
                 }
             }
 
+            // the MFMA stretches run at raised wave priority, so on a SIMD shared by two
+            // workgroups the matrix products of one take precedence over the softmax of
+            // the other, which fills the gaps
+            __builtin_amdgcn_s_setprio(0);
             const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
             softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
             l_run += tile_sum<NKB>(s);
+            __builtin_amdgcn_s_setprio(1);
 
             // O^T += V^T P^T, one key per lane half per MFMA: k-step r of block kb is
             // key kb*32 + 8*(r/4) + 4*h32 + r%4, the key the lane's S^T register r holds.
