@@ -18,7 +18,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kMaxDim = 128;
+constexpr int kMaxDim = 256;      // 16-bit forward
+constexpr int kMaxDim32 = 128;    // fp32 forward and the backward
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_num_cus[kMaxDevices];  // 0 = not queried yet
 
@@ -42,7 +43,7 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
     if (!mul_ok(B, H, &bh)) return FA_EINVAL;
     if (!mul_ok(bh, Nq, &t) || !mul_ok(t, d, &t)) return FA_EINVAL;
     if (!mul_ok(bh, Nk, &t) || !mul_ok(t, d, &t)) return FA_EINVAL;
-    if (d > kMaxDim) return FA_EUNSUPPORTED;
+    if (d > kMaxDim || (dtype == FA_F32 && d > kMaxDim32)) return FA_EUNSUPPORTED;
     // 32-bit index arithmetic inside one (batch, head): rows and row*d must fit.
     if (Nq * d > INT32_MAX || Nk * d > INT32_MAX) return FA_EUNSUPPORTED;
     if (B > INT32_MAX || H > INT32_MAX) return FA_EUNSUPPORTED;
@@ -68,7 +69,9 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // (bf16 d=128, N=128: 4.7 vs 2.8 TB/s on MI355X).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
-        if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > 512) {
+        if (d > 128) {
+            // head dims past 128: the 4-wave kernel, one wave per SIMD
+        } else if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > 512) {
             c.waves = 8;
             c.br = 256;
         } else if (!causal && c.dpad <= 96 && wgs128 < num_cus && Nk > 2 * c.bc) {
@@ -161,8 +164,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     const uintptr_t all16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
                             (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
     if (all16 % 2 != 0 || (uintptr_t)lse % 4 != 0 || (uintptr_t)delta % 4 != 0) return FA_EINVAL;
-    // the backward kernels exist for the 16-bit types on 16-byte rows only
-    if (dtype == FA_F32 || d % 8 != 0 || all16 % 16 != 0) return FA_EUNSUPPORTED;
+    // the backward kernels exist for the 16-bit types on 16-byte rows, d <= 128, only
+    if (dtype == FA_F32 || d % 8 != 0 || d > fa::kMaxDim32 || all16 % 16 != 0) return FA_EUNSUPPORTED;
     fa::BwdArgs a;
     a.q = q;
     a.k = k;

@@ -167,15 +167,17 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 // half merges them: m = max(m1, m2), l = l1 2^(m1-m) + l2 2^(m2-m), O likewise, the same
 // exact combination the online recurrence makes tile by tile.
 template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DP > 128 ? 1 : 2, DP > 128 ? 1 : 2)))
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
     static_assert(SPLIT == 1 || (SPLIT == 2 && !CAUSAL), "key split: non-causal only");
     constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB, BC = 64;
     constexpr int KST = DP + 8;   // K row stride (elements): 16-byte pad, conflict-free b128 reads
     // V row stride: 4 consecutive rows must start in 4 distinct quarters of the 16 bank groups
-    // (the transposed read serves 4 rows x 4 chunks at once): 20 or 12 chunks for d 128 / 64,
-    // the natural 12 or 4 chunks for d 96 / 32.
-    constexpr int VST = (DP == 128 || DP == 64) ? DP + 32 : DP;
+    // (the transposed read serves 4 rows x 4 chunks at once), i.e. a pitch of 4 or 12 chunks
+    // mod 16: head dims whose chunk count is a multiple of 8 (64, 128, 192, 256) get 4 pad
+    // chunks, the others (32, 96, 160, 224) already have one.
+    constexpr int VST = (DP / 8) % 8 == 0 ? DP + 32 : DP;
     constexpr int CPR = DP / 8;   // 16-byte chunks per row
     constexpr int CH = BC * CPR / (64 * NW);  // chunks per thread per tile
     static_assert(BC * CPR % (64 * NW) == 0, "tile load split");
@@ -858,9 +860,11 @@ static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st, int thread
 
 template <typename T, int DP>
 static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
-    if (cfg.waves == 8) {  // aligned, d % 8 == 0 (checked by the caller)
-        if (a.causal) return launch(fwd16_pp_kernel<T, DP, true>, a, cfg.br, st, 512);
-        return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
+    if constexpr (DP <= 128) {
+        if (cfg.waves == 8) {  // aligned, d % 8 == 0 (checked by the caller)
+            if (a.causal) return launch(fwd16_pp_kernel<T, DP, true>, a, cfg.br, st, 512);
+            return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
+        }
     }
     if (a.causal) {
         return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256)
@@ -895,6 +899,10 @@ int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) 
             case 64: return bf ? launch16<__bf16, 64>(a, cfg, vec, st) : launch16<_Float16, 64>(a, cfg, vec, st);
             case 96: return bf ? launch16<__bf16, 96>(a, cfg, vec, st) : launch16<_Float16, 96>(a, cfg, vec, st);
             case 128: return bf ? launch16<__bf16, 128>(a, cfg, vec, st) : launch16<_Float16, 128>(a, cfg, vec, st);
+            case 160: return bf ? launch16<__bf16, 160>(a, cfg, vec, st) : launch16<_Float16, 160>(a, cfg, vec, st);
+            case 192: return bf ? launch16<__bf16, 192>(a, cfg, vec, st) : launch16<_Float16, 192>(a, cfg, vec, st);
+            case 224: return bf ? launch16<__bf16, 224>(a, cfg, vec, st) : launch16<_Float16, 224>(a, cfg, vec, st);
+            case 256: return bf ? launch16<__bf16, 256>(a, cfg, vec, st) : launch16<_Float16, 256>(a, cfg, vec, st);
             default: return (int)hipErrorInvalidValue;
         }
     }

@@ -47,7 +47,8 @@ typedef enum {
     FA_OK = 0,
     FA_EINVAL = 1,       /* bad argument: null pointer, size < 1, unknown dtype,
                             non-finite scale, sizes whose products overflow    */
-    FA_EUNSUPPORTED = 2, /* valid request with no kernel for it (d > 128)      */
+    FA_EUNSUPPORTED = 2, /* valid request with no kernel for it (d > 256;      
+                            fp32 with d > 128)                              */
     FA_ELAUNCH = 3       /* the HIP runtime reported an error at launch        */
 } fa_status;
 
@@ -61,7 +62,7 @@ typedef enum {
  *          (fp32 accumulator rounded to nearest even)
  *   lse    [B, H, Nq] fp32 device buffer written in full: L = m + ln(l), the
  *          natural-log logsumexp of the scaled, masked scores of each row
- *   B, H, Nq, Nk, d   sizes, each >= 1; 1 <= d <= 128
+ *   B, H, Nq, Nk, d   sizes, each >= 1; d <= 256 for fp16/bf16, d <= 128 for fp32
  *   scale  multiplies q . k before the mask and the softmax; any finite value
  *          (0 and negative values included); 1/sqrt(d) is the usual choice
  *   causal 0: every key is visible. non-zero: key j is visible to query i iff

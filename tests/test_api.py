@@ -63,7 +63,8 @@ def test_invalid_arguments(L, kw):
     assert call(L, **kw) == fa.FA_EINVAL
 
 
-@pytest.mark.parametrize("kw", [dict(d=129), dict(d=256), dict(Nq=2**26, d=64), dict(Nk=2**25, d=128)])
+@pytest.mark.parametrize("kw", [dict(d=257), dict(d=512), dict(d=129, dtype=0), dict(d=256, dtype=0),
+                                dict(Nq=2**26, d=64), dict(Nk=2**25, d=128)])
 def test_unsupported(L, kw):
     assert call(L, **kw) == fa.FA_EUNSUPPORTED
 
@@ -86,11 +87,23 @@ def test_bwd_invalid_arguments(L, kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(d=129), dict(dtype=0), dict(d=60), dict(d=5), dict(q=P + 2), dict(dk=P + 8),
+    dict(d=136), dict(d=256), dict(dtype=0), dict(d=60), dict(d=5), dict(q=P + 2), dict(dk=P + 8),
 ])
 def test_bwd_unsupported(L, kw):
     """fp32, d not a multiple of 8 and 16-bit rows off 16-byte alignment have no backward kernel."""
     assert call_bwd(L, **kw) == fa.FA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [129, 160, 200, 224, 256])
+def test_select_config_large_head_dims(dtype, d):
+    """Head dims past 128 (16-bit only): the 4-wave kernel compiled for the padded dim."""
+    cfg = fa.fa_select_config(dtype, 4, 16, 4096, 4096, d, False)
+    assert cfg["waves"] == 4 and cfg["Br"] == 128 and cfg["Bc"] == 64
+    assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
+    vpad = 64 if (cfg["dpad"] // 8) % 8 == 0 else 0
+    lds = cfg["Bc"] * (cfg["dpad"] * 2 + 16) + cfg["Bc"] * (cfg["dpad"] * 2 + vpad)
+    assert lds <= 160 * 1024
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -147,7 +160,10 @@ def test_select_config_grid_fill(dtype):
 
 def test_select_config_errors():
     with pytest.raises(fa.FaError) as e:
-        fa.fa_select_config("bf16", 1, 1, 16, 16, 129, False)
+        fa.fa_select_config("bf16", 1, 1, 16, 16, 257, False)
+    assert e.value.status == fa.FA_EUNSUPPORTED
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_select_config("f32", 1, 1, 16, 16, 129, False)
     assert e.value.status == fa.FA_EUNSUPPORTED
     with pytest.raises(fa.FaError) as e:
         fa.fa_select_config("bf16", 0, 1, 16, 16, 64, False)

@@ -96,6 +96,12 @@ for dt in ("bf16", "f16", "f32"):
         for (Nq, Nk) in ((1, 1), (17, 63), (64, 65), (129, 127), (200, 1000), (300, 300)):
             for causal in (False, True):
                 SWEEP.append((dt, d, Nq, Nk, causal))
+# head dims past 128 (16-bit only)
+for dt in ("bf16", "f16"):
+    for d in (136, 160, 200, 256):
+        for (Nq, Nk) in ((1, 1), (129, 127), (200, 1000)):
+            for causal in (False, True):
+                SWEEP.append((dt, d, Nq, Nk, causal))
 
 
 @pytest.mark.parametrize("dt,d,Nq,Nk,causal", SWEEP)
