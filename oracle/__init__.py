@@ -149,3 +149,50 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool,
+                         threads: int | None = None):
+    """Exact attention forward over a packed batch of sequences of different lengths (fp64).
+
+    Page "Meta's xFormers has Attention kernel written in CUTLASS" (the grouped-GEMM
+    discussion) asks for fixed and variable sequence lengths in one kernel. Read plainly:
+    each sequence of the batch is its own attention problem, and sequences never see each
+    other's keys.
+
+    q: [H, Tq, d]; k, v: [H, Tk, d]; every head's rows hold the sequences back to back.
+    cu_q, cu_k: B+1 offsets, nondecreasing, from 0 to Tq (resp. Tk). Sequence b owns query
+    rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1]. The causal mask uses the
+    sequence's own positions (key j visible to query i iff j <= i, both counted from the
+    sequence start). A sequence with queries but no keys has an empty softmax sum: its
+    rows get O = 0 and L = ln 0 = -inf.
+
+    Each sequence goes through attention_fwd on its own slices. Returns O [H, Tq, d] and
+    L [H, Tq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or k.shape[0] != q.shape[0] \
+            or k.shape[2] != q.shape[2]:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    for name, cu, total in (("cu_q", cu_q, Tq), ("cu_k", cu_k, Tk)):
+        if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+            raise ValueError(f"{name} must run from 0 to {total} without decreasing")
+    if cu_q.size != cu_k.size:
+        raise ValueError("cu_q and cu_k must describe the same number of sequences")
+    o = np.zeros((H, Tq, d), dtype=np.float64)
+    lse = np.full((H, Tq), -np.inf, dtype=np.float64)
+    for b in range(cu_q.size - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe == qs or ke == ks:
+            continue  # no rows, or rows with an empty softmax (O = 0, L = -inf as set)
+        ob, lb = attention_fwd(q[None, :, qs:qe], k[None, :, ks:ke], v[None, :, ks:ke],
+                               scale, causal, threads=threads)
+        o[:, qs:qe] = ob[0]
+        lse[:, qs:qe] = lb[0]
+    return o, lse
