@@ -8,6 +8,8 @@ streams. There is no fallback: if the library is missing, the calls raise.
     fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict
     fa_status_str(code) -> str
     attention(q, k, v, scale=None, causal=False) -> (o, lse)  # allocates o and lse
+    fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max_q, max_k, scale, causal, stream=None)
+    attention_varlen(q, k, v, cu_q, cu_k, max_q=None, max_k=None, scale=None, causal=False)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale, causal, stream=None)
     attention_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
 """
@@ -23,7 +25,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
 DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
 
 _lock = threading.Lock()
@@ -61,6 +63,9 @@ def lib():
             L.fa_fwd.restype = ctypes.c_int
             L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                  ctypes.c_int, ctypes.c_int, vp]
+            L.fa_fwd_varlen.restype = ctypes.c_int
+            L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
             L.fa_bwd.restype = ctypes.c_int
             L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
@@ -141,6 +146,63 @@ def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     fa_fwd(q, k, v, o, lse, scale, causal, stream)
+    return o, lse
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max_q: int, max_k: int, scale: float, causal: bool,
+                  stream=None) -> None:
+    """Calls the C-ABI fa_fwd_varlen on packed sequences: q, o [H, Tq, d], k, v [H, Tk, d],
+    lse [H, Tq] float32, cu_q, cu_k int32 device tensors of B+1 offsets; max_q, max_k the
+    longest query and key sequence."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("cu_q", cu_q), ("cu_k", cu_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [H, total, d]")
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    if tuple(k.shape) != (H, Tk, d) or tuple(v.shape) != (H, Tk, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != (H, Tq, d) or tuple(lse.shape) != (H, Tq):
+        raise ValueError("o must be [H,Tq,d] and lse [H,Tq]")
+    if cu_q.dim() != 1 or cu_q.shape != cu_k.shape or cu_q.numel() < 2:
+        raise ValueError("cu_q and cu_k must be 1-D with B+1 entries each")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int32:
+        raise TypeError("cu_q and cu_k must be int32")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o must share one dtype; lse must be float32")
+    dev = q.device
+    if any(t.device != dev for t in (k, v, o, lse, cu_q, cu_k)):
+        raise ValueError("all tensors must be on one device")
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(dev):
+        rc = lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 cu_q.data_ptr(), cu_k.data_ptr(), cu_q.numel() - 1, H, Tq, Tk,
+                                 int(max_q), int(max_k), d, float(scale), int(bool(causal)),
+                                 _torch_dtype_code(q), handle)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_varlen")
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, max_q: int | None = None, max_k: int | None = None,
+                     scale: float | None = None, causal: bool = False, stream=None):
+    """Allocates o and lse and runs fa_fwd_varlen; returns (o, lse). Missing maxima are read
+    from the offsets (a device-to-host copy)."""
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    if max_q is None:
+        max_q = max(1, int((cu_q[1:] - cu_q[:-1]).max().item()))
+    if max_k is None:
+        max_k = max(1, int((cu_k[1:] - cu_k[:-1]).max().item()))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max_q, max_k, scale, causal, stream)
     return o, lse
 
 

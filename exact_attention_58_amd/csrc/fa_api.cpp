@@ -50,6 +50,12 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
     return FA_OK;
 }
 
+// Shared tail of fa_fwd and fa_fwd_varlen once the sizes are valid: alignment, tile choice,
+// launch. cu_q == nullptr selects the dense layout; otherwise Nq, Nk are the longest lengths.
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
+                  const int32_t* cu_k, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t tq,
+                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream);
+
 }  // namespace
 
 int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
@@ -86,6 +92,45 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
     *out = c;
     return FA_OK;
 }
+
+namespace {
+
+fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
+                  const int32_t* cu_k, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t tq,
+                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream) {
+    const int esz = dtype == FA_F32 ? 4 : 2;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % esz != 0 ||
+        (uintptr_t)lse % 4 != 0)
+        return FA_EINVAL;
+    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
+                     (d * esz) % 16 == 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
+    TileConfig cfg;
+    int rc = select_config(dtype, B, H, Nq, Nk, d, causal, dev_num_cus(dev), vec, &cfg);
+    if (rc != FA_OK) return (fa_status)rc;
+    FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = (int)B;
+    a.H = (int)H;
+    a.Nq = (int)Nq;
+    a.Nk = (int)Nk;
+    a.d = (int)d;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.causal = causal ? 1 : 0;
+    a.dtype = (int)dtype;
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.tq = tq;
+    a.tk = tk;
+    return launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
+}  // namespace
 
 }  // namespace fa
 
@@ -124,33 +169,29 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     if (!std::isfinite(scale)) return FA_EINVAL;
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
-    const int esz = dtype == FA_F32 ? 4 : 2;
-    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % esz != 0 ||
-        (uintptr_t)lse % 4 != 0)
-        return FA_EINVAL;
+    return fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
+                       stream);
+}
 
-    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
-                     (d * esz) % 16 == 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
-    fa::TileConfig cfg;
-    int rc = fa::select_config(dtype, B, H, Nq, Nk, d, causal, fa::dev_num_cus(dev), vec, &cfg);
-    if (rc != FA_OK) return (fa_status)rc;
-    fa::FwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
-    a.B = (int)B;
-    a.H = (int)H;
-    a.Nq = (int)Nq;
-    a.Nk = (int)Nk;
-    a.d = (int)d;
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    a.causal = causal ? 1 : 0;
-    a.dtype = (int)dtype;
-    return fa::launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B,
+                        int64_t H, int64_t total_q, int64_t total_k, int64_t max_seqlen_q,
+                        int64_t max_seqlen_k, int64_t d, float scale, int causal, fa_dtype dtype,
+                        void* stream) {
+    if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_EINVAL;
+    if (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) % 4 != 0) return FA_EINVAL;
+    if (!std::isfinite(scale)) return FA_EINVAL;
+    if (total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+        max_seqlen_q > total_q || max_seqlen_k > total_k)
+        return FA_EINVAL;
+    // every tensor as one (batch = 1, head) stack of `total` rows, and every sequence as a
+    // (batch, head) slice of the longest lengths: both must pass the dense limits
+    fa_status st = fa::check_args(dtype, B, H, max_seqlen_q, max_seqlen_k, d);
+    if (st != FA_OK) return st;
+    st = fa::check_args(dtype, 1, H, total_q, total_k, d);
+    if (st != FA_OK) return st;
+    return fa::run_fwd(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,
+                       total_q, total_k, d, scale, causal, dtype, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

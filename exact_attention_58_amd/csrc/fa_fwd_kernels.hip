@@ -44,6 +44,36 @@ namespace fa {
 // the unnormalised weights stay below 2^8.
 constexpr float kRescaleThreshold = 8.0f;
 
+// The rows of one (batch, head) pair. Dense inputs are [B,H,N,d]: pair bh starts at row bh*N
+// of every tensor. Packed sequences of different lengths (page "Meta's xFormers has Attention
+// kernel written in CUTLASS": fixed and variable lengths served by one kernel) are
+// [H, total, d]: sequence b of head h starts at row h*total + cu[b]. Offsets are clamped into
+// [0, total] and lengths to the launch's maxima, so offsets that break their documented
+// contract cannot move an access outside the tensors.
+struct Slice {
+    int64_t q0, k0;  // first query row and first key row of the pair
+    int nq, nk;      // its query and key counts
+};
+__device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a, int bh) {
+    if (a.cu_q == nullptr) return {(int64_t)bh * a.Nq, (int64_t)bh * a.Nk, a.Nq, a.Nk};
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int64_t qs = min(max((int64_t)a.cu_q[b], (int64_t)0), a.tq);
+    const int64_t qe = min(max((int64_t)a.cu_q[b + 1], qs), a.tq);
+    const int64_t ks = min(max((int64_t)a.cu_k[b], (int64_t)0), a.tk);
+    const int64_t ke = min(max((int64_t)a.cu_k[b + 1], ks), a.tk);
+    return {h * a.tq + qs, h * a.tk + ks, (int)min(qe - qs, (int64_t)a.Nq), (int)min(ke - ks, (int64_t)a.Nk)};
+}
+
+// Query rows [r0, r0 + br) of a sequence that has queries but no keys: the softmax sum is
+// empty, so O = 0 and L = ln 0 = -inf. Every thread of the workgroup takes part.
+template <typename E>
+__device__ void write_empty_rows(const FwdArgs& a, const Slice& sl, int r0, int br) {
+    const int rows = min(br, sl.nq - r0);
+    E* o = (E*)a.o + (sl.q0 + r0) * a.d;
+    for (int i = threadIdx.x; i < rows * a.d; i += blockDim.x) o[i] = E(0);
+    for (int i = threadIdx.x; i < rows; i += blockDim.x) a.lse[sl.q0 + r0 + i] = kNegInf;
+}
+
 // Maximum of the NKB*16 values of s as a balanced tree (v_max3), so the dependency chain is
 // logarithmic in the number of values instead of linear. MIN selects the minimum instead.
 template <int NKB, bool MIN>
@@ -200,14 +230,17 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int bh = wg / n_qtiles;
     int qt = wg - bh * n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
-    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const Slice sl = slice_of(a, bh);
+    const int Nq = sl.nq, Nk = sl.nk, d = a.d;
     const int q0 = qt * BR;
+    if (q0 >= Nq) return;  // a packed sequence shorter than the longest
+    if (Nk == 0) return write_empty_rows<uint16_t>(a, sl, q0, BR);
     const int r0w = q0 + rbk * 32;
     const int myq = r0w + l32;
 
-    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
-    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
-    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+    const uint16_t* qg = (const uint16_t*)a.q + sl.q0 * d;
+    const uint16_t* kg = (const uint16_t*)a.k + sl.k0 * d;
+    const uint16_t* vg = (const uint16_t*)a.v + sl.k0 * d;
 
     // Q fragments (B operand of S^T = K Q^T): lane holds Q[myq][16*ds + 8*h32 + 0..7]
     u32x4 qf[NDS];
@@ -335,7 +368,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const float l_tot = wave_half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (myq < Nq) {
-        uint16_t* og = (uint16_t*)a.o + ((int64_t)bh * Nq + myq) * d;
+        uint16_t* og = (uint16_t*)a.o + (sl.q0 + myq) * d;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -355,7 +388,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
                     if (d0 + 3 < d) og[d0 + 3] = Half<T>::one(o3);
                 }
             }
-        if (h32 == 0) a.lse[(int64_t)bh * Nq + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (h32 == 0) a.lse[sl.q0 + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -420,14 +453,17 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int bh = wg / n_qtiles;
     int qt = wg - bh * n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
-    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const Slice sl = slice_of(a, bh);
+    const int Nq = sl.nq, Nk = sl.nk, d = a.d;
     const int q0 = qt * BR;
+    if (q0 >= Nq) return;  // a packed sequence shorter than the longest
+    if (Nk == 0) return write_empty_rows<uint16_t>(a, sl, q0, BR);
     const int r0w = q0 + grp * 32 * WPG + wig * 32;
     const int myq = r0w + l32;
 
-    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
-    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
-    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+    const uint16_t* qg = (const uint16_t*)a.q + sl.q0 * d;
+    const uint16_t* kg = (const uint16_t*)a.k + sl.k0 * d;
+    const uint16_t* vg = (const uint16_t*)a.v + sl.k0 * d;
 
     u32x4 qf[NDS];
 #pragma unroll
@@ -646,7 +682,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const float l_tot = wave_half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (myq < Nq) {
-        uint16_t* og = (uint16_t*)a.o + ((int64_t)bh * Nq + myq) * d;
+        uint16_t* og = (uint16_t*)a.o + (sl.q0 + myq) * d;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -658,7 +694,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
                     *(u32x2*)(og + d0) = w;
                 }
             }
-        if (h32 == 0) a.lse[(int64_t)bh * Nq + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (h32 == 0) a.lse[sl.q0 + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 
@@ -708,14 +744,17 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const int bh = wg / n_qtiles;
     int qt = wg - bh * n_qtiles;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
-    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const Slice sl = slice_of(a, bh);
+    const int Nq = sl.nq, Nk = sl.nk, d = a.d;
     const int q0 = qt * BR;
+    if (q0 >= Nq) return;  // a packed sequence shorter than the longest
+    if (Nk == 0) return write_empty_rows<float>(a, sl, q0, BR);
     const int r0w = q0 + wave * 32;
     const int myq = r0w + l32;
 
-    const float* qg = (const float*)a.q + (int64_t)bh * Nq * d;
-    const float* kg = (const float*)a.k + (int64_t)bh * Nk * d;
-    const float* vg = (const float*)a.v + (int64_t)bh * Nk * d;
+    const float* qg = (const float*)a.q + sl.q0 * d;
+    const float* kg = (const float*)a.k + sl.k0 * d;
+    const float* vg = (const float*)a.v + sl.k0 * d;
 
     // Q: lane holds Q[myq][h32*HALF + 0..HALF-1]
     float qf[HALF];
@@ -828,7 +867,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const float l_tot = wave_half_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (myq < Nq) {
-        float* og = (float*)a.o + ((int64_t)bh * Nq + myq) * d;
+        float* og = (float*)a.o + (sl.q0 + myq) * d;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -844,7 +883,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
                         if (d0 + e < d) og[d0 + e] = w[e];
                 }
             }
-        if (h32 == 0) a.lse[(int64_t)bh * Nq + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+        if (h32 == 0) a.lse[sl.q0 + myq] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
     }
 }
 

@@ -13,10 +13,15 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int B, H, Nq, Nk, d;
+    int B, H, Nq, Nk, d;  // packed sequences: Nq, Nk are the longest lengths
     float scale_log2;  // softmax scale times log2(e): scores enter exp2 directly
     int causal;
     int dtype;         // fa_dtype value
+    // Packed sequences of different lengths (null for the dense [B,H,N,d] layout): device
+    // offsets, B+1 each; tensors are [H, tq, d] (keys [H, tk, d]), lse is [H, tq].
+    const int* cu_q;
+    const int* cu_k;
+    int64_t tq, tk;
 };
 
 // Tile configuration chosen by the selector.

@@ -96,3 +96,18 @@ def make_random(shape, dtype: str, seed: int, std: float = 1.0):
     if std != 1.0:
         x = x * std
     return x.to(DTYPES[dtype]).contiguous()
+
+
+def make_lengths(n: int, lo: int, hi: int, seed: int):
+    """Seeded sequence lengths for packed batches: n integers drawn uniformly from [lo, hi]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return [int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g)]
+
+
+def offsets(lengths):
+    """B+1 int32 offsets (0, l0, l0+l1, ...) of back-to-back sequences."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32)

@@ -87,6 +87,51 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
+ * fa_fwd_varlen -- attention forward over a packed batch of sequences of different
+ * lengths in one launch, asynchronous on `stream`.
+ *
+ * Page "Meta's xFormers has Attention kernel written in CUTLASS" (the grouped-GEMM
+ * discussion) asks for fixed and variable sequence lengths served by one kernel. Each
+ * sequence is its own attention problem: its queries see only its own keys, and the causal
+ * mask counts positions from the sequence's start (key j visible to query i iff j <= i).
+ * A sequence with queries but no keys has an empty softmax sum: its rows get O = 0 and
+ * L = -inf.
+ *
+ * Arguments
+ *   q, o   [H, total_q, d] device buffers, row-major, element type `dtype`: every head
+ *          holds the B sequences' query rows back to back
+ *   k, v   [H, total_k, d] device buffers, row-major, likewise for the key rows
+ *   lse    [H, total_q] fp32 device buffer
+ *   cu_seqlens_q, cu_seqlens_k   device int32 arrays of B+1 offsets: sequence b owns query
+ *          rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ *          cu_seqlens_k[b+1]-1 of every head. They must start at 0, never decrease, end at
+ *          total_q (resp. total_k), and no sequence may be longer than max_seqlen_q (resp.
+ *          max_seqlen_k). Zero-length sequences are allowed.
+ *   B      number of sequences (>= 1)
+ *   H, d, scale, causal, dtype, stream   as for fa_fwd
+ *   total_q, total_k           rows per head (>= 1)
+ *   max_seqlen_q, max_seqlen_k the longest query and key sequence (1 .. total); they set
+ *          the grid, which has a workgroup for every (query tile of the longest sequence,
+ *          head, sequence); tiles past a sequence's end return at once.
+ *
+ * The offsets live on the device, so the library cannot check them without a
+ * synchronisation and does not: offsets that break the rules above give unspecified
+ * values in o and lse (the kernels clamp every offset into [0, total] and every length to
+ * its maximum, so no access leaves the buffers). Rows of o and lse that belong to no
+ * sequence are not written.
+ *
+ * Ownership and errors: as fa_fwd. FA_EINVAL also for null or misaligned offset arrays and
+ * for totals or maxima below 1 or maxima above their totals; FA_EUNSUPPORTED for sizes whose
+ * dense equivalent (B sequences of the maximum lengths, or one batch of the totals) fa_fwd
+ * would reject.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int64_t B, int64_t H, int64_t total_q, int64_t total_k,
+                        int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t d,
+                        float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
  * fa_bwd -- gradients of the attention forward, asynchronous on `stream`.
  *
  * Given the forward's inputs q, k, v, its outputs o and lse (as fa_fwd wrote them, same

@@ -28,7 +28,8 @@ def header_functions():
 
 def test_header_symbols_are_exported(L):
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_status_str", "fa_select_config",
+                          "fa_version"}
     for n in names:
         assert hasattr(L, n), n
     assert set(fa.EXPORTED) == set(names)
@@ -67,6 +68,28 @@ def test_invalid_arguments(L, kw):
                                 dict(Nq=2**26, d=64), dict(Nk=2**25, d=128)])
 def test_unsupported(L, kw):
     assert call(L, **kw) == fa.FA_EUNSUPPORTED
+
+
+def call_varlen(L, q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, H=1, Tq=8, Tk=8, mq=4, mk=4, d=64,
+                scale=0.125, causal=0, dtype=2):
+    return L.fa_fwd_varlen(q, k, v, o, lse, cq, ck, B, H, Tq, Tk, mq, mk, d, ctypes.c_float(scale),
+                           causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(o=None), dict(lse=None), dict(cq=None), dict(ck=None),
+    dict(cq=P + 2), dict(ck=P + 1), dict(q=P + 1),
+    dict(B=0), dict(H=0), dict(Tq=0), dict(Tk=0), dict(mq=0), dict(mk=0), dict(d=0),
+    dict(mq=9), dict(mk=9), dict(dtype=5), dict(scale=float("nan")),
+    dict(B=2**40, H=2**40),
+])
+def test_varlen_invalid_arguments(L, kw):
+    assert call_varlen(L, **kw) == fa.FA_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(d=257), dict(d=129, dtype=0), dict(Tq=2**26, mq=2**26, d=64)])
+def test_varlen_unsupported(L, kw):
+    assert call_varlen(L, **kw) == fa.FA_EUNSUPPORTED
 
 
 def call_bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, delta=P, B=1, H=1, Nq=8, Nk=8, d=64,

@@ -1,0 +1,123 @@
+"""GPU parity of the packed variable-length forward (fa_fwd_varlen through the C ABI) against
+the fp64 oracle (oracle.attention_fwd_varlen).
+
+Tolerances as for the dense forward: O max-abs <= 1e-4 (fp32) and <= 2e-2 (fp16/bf16), L
+max-abs <= 1e-3. Rows of a sequence that has queries but no keys must hold exactly O = 0 and
+L = -inf. The cases cover every kernel the selector can pick for packed input (ping-pong,
+4-wave with and without the key split, fp32, unaligned rows), zero-length sequences, single
+rows, lengths that end inside a tile, and causal masks in per-sequence positions.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_58_amd as fa
+import oracle
+from exact_attention_58_amd.workloads import make_lengths, make_random, offsets
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+TOL_L = 1e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.ensure_built()
+    fa.lib()
+
+
+def run_case(dt, H, lq, lk, d, causal, seed, scale=None, heads=None, expect_waves=None):
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    Tq, Tk = sum(lq), sum(lk)
+    q = make_random((H, Tq, d), dt, seed)
+    k = make_random((H, Tk, d), dt, seed + 1)
+    v = make_random((H, Tk, d), dt, seed + 2)
+    cu_q, cu_k = offsets(lq), offsets(lk)
+    what = f"{dt} H={H} lq={lq if len(lq) < 12 else str(len(lq)) + ' seqs'} lk=... d={d} causal={causal}"
+    if expect_waves is not None:
+        cfg = fa.fa_select_config(dt, len(lq), H, max(lq), max(lk), d, causal)
+        assert cfg["waves"] == expect_waves, (what, cfg)
+    say(f"  varlen {what}")
+    o, lse = fa.attention_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(),
+                                 max(1, max(lq)), max(1, max(lk)), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    if heads is not None:
+        q, k, v, o, lse = q[heads], k[heads], v[heads], o[heads], lse[heads]
+    o_ref, l_ref = oracle.attention_fwd_varlen(q.double(), k.double(), v.double(), cu_q.numpy(),
+                                               cu_k.numpy(), scale, causal)
+    empty = ~np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(lse), ~empty), what
+    assert np.all(lse[empty] == -np.inf) and np.all(o[empty] == 0.0), what
+    assert np.all(np.isfinite(o)), what
+    o_err = float(np.max(np.abs(o - o_ref)))
+    l_err = float(np.max(np.abs(lse[~empty] - l_ref[~empty]), initial=0.0))
+    say(f"    max|dO|={o_err:.3e}  max|dL|={l_err:.3e}")
+    assert o_err <= TOL_O[dt], what
+    assert l_err <= TOL_L, what
+
+
+MIXES = [
+    ([1, 17, 300, 0, 129], [5, 64, 300, 0, 128]),
+    ([64, 65, 63], [200, 1, 63]),
+    ([130, 7], [0, 260]),            # queries with no keys
+    ([257], [1000]),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("d", [40, 64, 128])
+@pytest.mark.parametrize("mix", range(len(MIXES)))
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_mixes(dt, d, mix, causal):
+    lq, lk = MIXES[mix]
+    run_case(dt, 2, lq, lk, d, causal, seed=500 + 11 * mix + d)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [36, 96, 200, 256])
+def test_varlen_other_head_dims(dt, d):
+    run_case(dt, 2, [70, 0, 190], [33, 5, 190], d, True, seed=900 + d)
+    run_case(dt, 2, [70, 0, 190], [33, 5, 190], d, False, seed=901 + d)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_pingpong_kernel(causal):
+    """Long sequences on many heads: the 256-row ping-pong kernel (heads 0 and 15 checked)."""
+    lq = [1024, 700, 513, 1, 999, 256, 0, 800]
+    run_case("bf16", 16, lq, lq, 128, causal, seed=41, heads=[0, 15], expect_waves=8)
+
+
+def test_varlen_key_split_kernel():
+    """A small non-causal grid at d <= 96: the 64-row kernel with the two-way key split."""
+    run_case("f16", 2, [300, 200], [700, 129], 64, False, seed=43, expect_waves=4)
+    cfg = fa.fa_select_config("f16", 2, 2, 300, 700, 64, False)
+    assert cfg["Br"] == 64
+
+
+def test_varlen_many_sequences():
+    """A seeded length mix of 64 sequences, causal, d=64."""
+    lq = make_lengths(64, 1, 400, seed=7)
+    run_case("bf16", 4, lq, lq, 64, True, seed=47)
+
+
+def test_varlen_equal_lengths_match_dense():
+    """Equal lengths: the packed result equals the dense fa_fwd result on the same data."""
+    B, H, N, d = 3, 4, 333, 64
+    q, k, v = (make_random((B, H, N, d), "bf16", 60 + i).cuda() for i in range(3))
+    o_dense, l_dense = fa.attention(q, k, v, causal=True)
+    pack = lambda t: t.transpose(0, 1).reshape(H, B * N, *t.shape[3:]).contiguous()
+    cu = offsets([N] * B).cuda()
+    o, lse = fa.attention_varlen(pack(q), pack(k), pack(v), cu, cu, N, N, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, pack(o_dense)) and torch.equal(lse, pack(l_dense))
