@@ -110,6 +110,39 @@ def time_backward(fa, torch, w, steps, warmup):
     return ms
 
 
+def time_varlen(fa, torch, causal, steps, warmup):
+    """Packed batch of 16 bf16 sequences (lengths seeded uniform in [512, 4096], same for
+    queries and keys), H=16, d=128, through fa_fwd_varlen. FLOP: the sum over sequences of
+    4*H*n*n*d, halved for causal. Returns (description, ms per call, TFLOP/s)."""
+    from exact_attention_58_amd.workloads import make_lengths, make_random, offsets
+    dev = torch.device("cuda:0")
+    H, d = 16, 128
+    lens = make_lengths(16, 512, 4096, seed=77)
+    T = sum(lens)
+    q, k, v = (make_random((H, T, d), "bf16", 700 + i).to(dev) for i in range(3))
+    cu = offsets(lens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    scale = 1.0 / d ** 0.5
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: fa.fa_fwd_varlen(q, k, v, o, lse, cu, cu, max(lens), max(lens), scale, causal, stream)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(4.0 * H * n * n * d for n in lens) / (2 if causal else 1)
+    desc = f"16 sequences, lengths {min(lens)}..{max(lens)} (total {T}), H={H} d={d} bf16"
+    del q, k, v, o, lse
+    return desc, ms, flops / (ms * 1e-3) / 1e12
+
+
 def roofline_for(w, ev_ms, sha):
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -271,6 +304,16 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
                                       "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None}})
             log(f"  {name} backward: {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of {ow.dtype} peak)")
+        # packed sequences of different lengths in one launch
+        for causal in (False, True):
+            desc, ms, tf = time_varlen(fa, torch, causal, max(5, min(args.steps, 20)), 2)
+            peak = PEAK_TFLOPS["bf16"]
+            name = f"varlen_bf16{'_causal' if causal else ''}"
+            also.append({"workload": name, "shape": desc, "dtype": "bf16", "causal": causal,
+                         "ms_per_step": round(ms, 4), "tflops": round(tf, 2),
+                         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                                      "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None}})
+            log(f"  {name} ({desc}): {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of bf16 peak)")
         sweep, copy_gbs = hbm_sweep(fa, torch, args.steps)
         for s in sweep:
             log(f"  short N={s['N']}: {s['GB_per_s']} GB/s ({100 * s['hbm_frac']:.1f}% of 8 TB/s)")

@@ -64,6 +64,27 @@ __device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a
     return {h * a.tq + qs, h * a.tk + ks, (int)min(qe - qs, (int64_t)a.Nq), (int)min(ke - ks, (int64_t)a.Nk)};
 }
 
+// Workgroup -> (batch-head pair, query tile). Workgroups are dealt to the 8 XCDs in turn.
+// Dense inputs give every pair the same work, so each XCD takes a contiguous run of pairs
+// (xcd_remap) and keeps their K and V in its own L2. Packed sequences give each pair work in
+// proportion to its sequence's length, and contiguous runs would load one XCD with the
+// longest sequences; there pair p goes to XCD p % 8 with all its query tiles, which spreads
+// every sequence's heads over all XCDs (a bijection when the pair count is a multiple of 8,
+// otherwise the dense order is kept).
+struct TileId {
+    int bh, qt;
+};
+__device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles) {
+    const int i = blockIdx.x;
+    if (a.cu_q != nullptr && (a.B * a.H) % 8 == 0) {
+        const int k = i >> 3, m = k / n_qtiles;
+        return {(i & 7) + 8 * m, k - m * n_qtiles};
+    }
+    const int wg = xcd_remap(i, gridDim.x);
+    const int bh = wg / n_qtiles;
+    return {bh, wg - bh * n_qtiles};
+}
+
 // Query rows [r0, r0 + br) of a sequence that has queries but no keys: the softmax sum is
 // empty, so O = 0 and L = ln 0 = -inf. Every thread of the workgroup takes part.
 template <typename E>
@@ -226,9 +247,9 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / n_qtiles;
-    int qt = wg - bh * n_qtiles;
+    const TileId wt = tile_of(a, n_qtiles);
+    const int bh = wt.bh;
+    int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
     const Slice sl = slice_of(a, bh);
     const int Nq = sl.nq, Nk = sl.nk, d = a.d;
@@ -449,9 +470,9 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int grp = wave / WPG, wig = wave % WPG;
 
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / n_qtiles;
-    int qt = wg - bh * n_qtiles;
+    const TileId wt = tile_of(a, n_qtiles);
+    const int bh = wt.bh;
+    int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
     const Slice sl = slice_of(a, bh);
     const int Nq = sl.nq, Nk = sl.nk, d = a.d;
@@ -740,9 +761,9 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
 
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / n_qtiles;
-    int qt = wg - bh * n_qtiles;
+    const TileId wt = tile_of(a, n_qtiles);
+    const int bh = wt.bh;
+    int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
     const Slice sl = slice_of(a, bh);
     const int Nq = sl.nq, Nk = sl.nk, d = a.d;
