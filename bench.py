@@ -34,12 +34,12 @@ KERNEL_SRC = os.path.join(ROOT, "exact_attention_58_amd", "csrc", "fa_fwd_kernel
 # counters), keyed by workload, valid only for the kernel source whose sha256 prefix is
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
-    # profiles/fwd32_pages_f32.txt: FETCH_SIZE 24643.9 KiB x 2.0 + WRITE_SIZE 16640 KiB x 1.0
-    "pages_f32": {"bytes": 67510067, "kernel_sha": "0e11a9925fe954bc"},
-    # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE 98396.8 KiB x 2.0 + WRITE_SIZE 66560 KiB x 1.0
-    "d128_bf16": {"bytes": 269674086, "kernel_sha": "0e11a9925fe954bc"},
-    # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE 29761 KiB x 2.0 + WRITE_SIZE 16896 KiB x 1.0
-    "long_causal_bf16": {"bytes": 78252032, "kernel_sha": "0e11a9925fe954bc"},
+    # profiles/fwd32_pages_f32.txt: FETCH_SIZE 24654 KiB x 2.0 + WRITE_SIZE 16640 KiB x 1.0
+    "pages_f32": {"bytes": 67530688, "kernel_sha": "b4c8f54041b8a009"},
+    # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE 98406.8 KiB x 2.0 + WRITE_SIZE 66560 KiB x 1.0
+    "d128_bf16": {"bytes": 269694549, "kernel_sha": "b4c8f54041b8a009"},
+    # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE 29775.4 KiB x 2.0 + WRITE_SIZE 16896 KiB x 1.0
+    "long_causal_bf16": {"bytes": 78281472, "kernel_sha": "b4c8f54041b8a009"},
 }
 
 
