@@ -143,6 +143,46 @@ def time_varlen(fa, torch, causal, steps, warmup):
     return desc, ms, flops / (ms * 1e-3) / 1e12
 
 
+def tune_table(fa, torch, steps):
+    """fa_tune_fwd on a few problems off the headline set: the built-in tile choice and the
+    tuned one, each timed over `steps` launches with HIP events (the record is cleared after)."""
+    from exact_attention_58_amd.workloads import Workload, make_inputs
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    probs = [Workload("tune_d128_N1024", 16, 16, 1024, 1024, 128, "bf16", False, seed=31),
+             Workload("tune_d64_N2048_causal", 2, 8, 2048, 2048, 64, "bf16", True, seed=32),
+             Workload("tune_d96_ragged", 2, 12, 1000, 3001, 96, "f16", False, seed=33, std=0.5),
+             Workload("tune_d128_N8192_causal", 1, 16, 8192, 8192, 128, "bf16", True, seed=34)]
+    out = []
+    stream = torch.cuda.current_stream(dev)
+    for w in probs:
+        q, k, v = (t.to(dev) for t in make_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
+        rule = fa.fa_select_config(w.dtype, w.B, w.H, w.Nq, w.Nk, w.d, w.causal, num_cus=cus)
+        rule = {x: rule[x] for x in ("Br", "Bc", "waves")}
+        best = fa.fa_tune_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, reps=max(3, steps // 5))
+        times = {}
+        for name, cfg in (("built_in", rule), ("tuned", best)):
+            for _ in range(2):
+                fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            times[name] = e0.elapsed_time(e1) / steps
+        out.append({"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                    "dtype": w.dtype, "causal": w.causal, "built_in": rule, "tuned": best,
+                    "built_in_ms": round(times["built_in"], 4), "tuned_ms": round(times["tuned"], 4),
+                    "tuned_tflops": round(w.flops / (times["tuned"] * 1e-3) / 1e12, 1)})
+        del q, k, v, o, lse
+    fa.fa_tune_clear()
+    return out
+
+
 def roofline_for(w, ev_ms, sha):
     achieved = w.flops / (ev_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
@@ -279,7 +319,7 @@ def main():
     log(f"  {w.name}: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/launch (events), {tflops:.1f} TFLOP/s")
 
     also = []
-    sweep, copy_gbs = None, None
+    sweep, copy_gbs, tuned = None, None, None
     if not args.quick:
         for name, ow in WORKLOADS.items():
             if name == w.name:
@@ -314,6 +354,10 @@ def main():
                          "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
                                       "unit": "TFLOP/s", "frac": round(tf / peak, 4), "traffic": None}})
             log(f"  {name} ({desc}): {ms:.3f} ms, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of bf16 peak)")
+        tuned = tune_table(fa, torch, max(5, min(args.steps, 20)))
+        for t in tuned:
+            log(f"  {t['workload']}: built-in {t['built_in']} {t['built_in_ms']} ms, tuned {t['tuned']} "
+                f"{t['tuned_ms']} ms ({t['tuned_tflops']} TFLOP/s)")
         sweep, copy_gbs = hbm_sweep(fa, torch, args.steps)
         for s in sweep:
             log(f"  short N={s['N']}: {s['GB_per_s']} GB/s ({100 * s['hbm_frac']:.1f}% of 8 TB/s)")
@@ -347,6 +391,7 @@ def main():
         "cpu_baseline": cpu,
         "also": also,
         "hbm_sweep": {"runs": sweep, "device_copy_GB_per_s": copy_gbs} if sweep else None,
+        "autotune": tuned,
         "device": {"name": props.name, "cus": props.multi_processor_count},
         "kernel_sha": sha,
     }

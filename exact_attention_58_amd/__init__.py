@@ -8,6 +8,9 @@ streams. There is no fallback: if the library is missing, the calls raise.
     fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict
     fa_status_str(code) -> str
     attention(q, k, v, scale=None, causal=False) -> (o, lse)  # allocates o and lse
+    fa_fwd_config(q, k, v, o, lse, scale, causal, cfg, stream=None)   # cfg: {"Br","Bc","waves"}
+    fa_tune_fwd(q, k, v, o, lse, scale, causal, reps=10, stream=None) -> cfg dict
+    fa_tune_clear()
     fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, max_q, max_k, scale, causal, stream=None)
     attention_varlen(q, k, v, cu_q, cu_k, max_q=None, max_k=None, scale=None, causal=False)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale, causal, stream=None)
@@ -25,7 +28,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
 DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
 
 _lock = threading.Lock()
@@ -66,6 +69,16 @@ def lib():
             L.fa_fwd_varlen.restype = ctypes.c_int
             L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64,
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+            L.fa_fwd_config.restype = ctypes.c_int
+            L.fa_fwd_config.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, vp]
+            ip_ = ctypes.POINTER(ctypes.c_int)
+            L.fa_tune_fwd.restype = ctypes.c_int
+            L.fa_tune_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ip_, ip_, ip_]
+            L.fa_tune_clear.restype = None
+            L.fa_tune_clear.argtypes = []
             L.fa_bwd.restype = ctypes.c_int
             L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
@@ -136,6 +149,68 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
                           handle)
     if rc != FA_OK:
         raise FaError(rc)
+
+
+def _check_dense(q, k, v, o, lse):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B,H,N,d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(o.shape) != (B, H, Nq, d) or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("o must be [B,H,Nq,d] and lse [B,H,Nq]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype) or lse.dtype != torch.float32:
+        raise TypeError("q, k, v, o must share one dtype; lse must be float32")
+    if any(t.device != q.device for t in (k, v, o, lse)):
+        raise ValueError("all tensors must be on one device")
+    return B, H, Nq, Nk, d
+
+
+def _stream_handle(stream, dev):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def fa_fwd_config(q, k, v, o, lse, scale: float, causal: bool, cfg: dict, stream=None) -> None:
+    """fa_fwd with an explicit tile configuration (a dict with Br, Bc, waves)."""
+    import torch
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        rc = lib().fa_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
+                                 int(cfg["Br"]), int(cfg["Bc"]), int(cfg["waves"]), handle)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_fwd_config")
+
+
+def fa_tune_fwd(q, k, v, o, lse, scale: float, causal: bool, reps: int = 10, stream=None) -> dict:
+    """Times every tile configuration for this problem, records the fastest for later fa_fwd
+    calls on the same problem and returns it (blocks until the timed launches finish)."""
+    import torch
+    B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
+    handle = _stream_handle(stream, q.device)
+    out = [ctypes.c_int(0) for _ in range(3)]
+    with torch.cuda.device(q.device):
+        rc = lib().fa_tune_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                               B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
+                               int(reps), handle, *[ctypes.byref(x) for x in out])
+    if rc != FA_OK:
+        raise FaError(rc, "fa_tune_fwd")
+    return dict(zip(("Br", "Bc", "waves"), (x.value for x in out)))
+
+
+def fa_tune_clear() -> None:
+    lib().fa_tune_clear()
 
 
 def attention(q, k, v, scale: float | None = None, causal: bool = False, stream=None):

@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -50,11 +51,70 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
     return FA_OK;
 }
 
+// Whether `cfg` names a kernel that exists for these inputs: the 16-bit kernels are the
+// ping-pong kernel (8 waves, 256 rows: 16-byte rows, d % 8 == 0, d <= 128), the 4-wave kernel
+// (128 rows) and its key-split form (64 rows: non-causal, d <= 96); fp32 has one kernel per
+// head dim. The tile keys and the padded head dim are fixed by dtype and d.
+bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool aligned) {
+    const int dpad = (int)((d + 31) / 32) * 32;
+    if (cfg.dpad != dpad) return false;
+    if (dtype == FA_F32) return cfg.waves == 4 && cfg.br == 128 && cfg.bc == (dpad > 96 ? 32 : 64);
+    if (cfg.bc != 64) return false;
+    if (cfg.waves == 8) return cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
+    if (cfg.waves != 4) return false;
+    if (cfg.br == 128) return true;
+    return cfg.br == 64 && !causal && dpad <= 96;
+}
+
+// Configurations fa_tune_fwd measured fastest, one per exact problem (device, dtype, sizes,
+// causal flag). Bounded: when full, the oldest entry is replaced.
+struct TuneKey {
+    int dev, dtype, causal;
+    int64_t B, H, Nq, Nk, d;
+    bool operator==(const TuneKey& o) const {
+        return dev == o.dev && dtype == o.dtype && causal == o.causal && B == o.B && H == o.H &&
+               Nq == o.Nq && Nk == o.Nk && d == o.d;
+    }
+};
+constexpr int kTuneSlots = 256;
+std::mutex g_tune_mu;
+TuneKey g_tune_key[kTuneSlots];
+TileConfig g_tune_cfg[kTuneSlots];
+int g_tune_used = 0, g_tune_next = 0;
+std::atomic<int> g_tune_count{0};  // lets fa_fwd skip the lock while nothing is tuned
+
+bool tuned_lookup(const TuneKey& k, TileConfig* out) {
+    if (g_tune_count.load(std::memory_order_acquire) == 0) return false;
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    for (int i = 0; i < g_tune_used; ++i)
+        if (g_tune_key[i] == k) {
+            *out = g_tune_cfg[i];
+            return true;
+        }
+    return false;
+}
+void tuned_store(const TuneKey& k, const TileConfig& cfg) {
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    for (int i = 0; i < g_tune_used; ++i)
+        if (g_tune_key[i] == k) {
+            g_tune_cfg[i] = cfg;
+            return;
+        }
+    int slot = g_tune_used < kTuneSlots ? g_tune_used++ : g_tune_next;
+    if (g_tune_used == kTuneSlots && slot == g_tune_next) g_tune_next = (g_tune_next + 1) % kTuneSlots;
+    g_tune_key[slot] = k;
+    g_tune_cfg[slot] = cfg;
+    g_tune_count.store(g_tune_used, std::memory_order_release);
+}
+
 // Shared tail of fa_fwd and fa_fwd_varlen once the sizes are valid: alignment, tile choice,
 // launch. cu_q == nullptr selects the dense layout; otherwise Nq, Nk are the longest lengths.
+// `force` (may be null): launch this configuration instead of the selector's, or fail with
+// FA_EUNSUPPORTED when no kernel of that shape exists for these inputs.
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
                   const int32_t* cu_k, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t tq,
-                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream);
+                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream,
+                  const TileConfig* force = nullptr, TileConfig* used = nullptr);
 
 }  // namespace
 
@@ -97,18 +157,31 @@ namespace {
 
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
                   const int32_t* cu_k, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t tq,
-                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream) {
+                  int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream,
+                  const TileConfig* force, TileConfig* used) {
     const int esz = dtype == FA_F32 ? 4 : 2;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % esz != 0 ||
         (uintptr_t)lse % 4 != 0)
         return FA_EINVAL;
     const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
                      (d * esz) % 16 == 0;
+    if (force && !config_ok(*force, dtype, d, causal, vec)) return FA_EUNSUPPORTED;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
     TileConfig cfg;
     int rc = select_config(dtype, B, H, Nq, Nk, d, causal, dev_num_cus(dev), vec, &cfg);
     if (rc != FA_OK) return (fa_status)rc;
+    if (force) {
+        cfg = *force;
+    } else if (cu_q == nullptr) {
+        TileConfig t;
+        if (tuned_lookup(TuneKey{dev, (int)dtype, causal ? 1 : 0, B, H, Nq, Nk, d}, &t) &&
+            config_ok(t, dtype, d, causal, vec))
+            cfg = t;
+    }
+    // the grid of a forced or tuned tile height must stay within the launch limit too
+    if ((Nq + cfg.br - 1) / cfg.br * B * H > INT32_MAX) return FA_EUNSUPPORTED;
+    if (used) *used = cfg;
     FwdArgs a{};
     a.q = q;
     a.k = k;
@@ -192,6 +265,89 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
     if (st != FA_OK) return st;
     return fa::run_fwd(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, max_seqlen_q, max_seqlen_k,
                        total_q, total_k, d, scale, causal, dtype, stream);
+}
+
+fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                        int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                        fa_dtype dtype, int Br, int Bc, int waves, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
+    if (!std::isfinite(scale)) return FA_EINVAL;
+    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    fa::TileConfig cfg{Br, Bc, waves, (int)((d + 31) / 32) * 32};
+    return fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
+                       stream, &cfg);
+}
+
+fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
+                      fa_dtype dtype, int reps, void* stream, int* Br, int* Bc, int* waves) {
+    if (!q || !k || !v || !o || !lse) return FA_EINVAL;
+    if (!std::isfinite(scale) || reps < 1 || reps > 1000) return FA_EINVAL;
+    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    const int dpad = (int)((d + 31) / 32) * 32;
+    const fa::TileConfig cand[4] = {{256, 64, 8, dpad}, {128, 64, 4, dpad}, {64, 64, 4, dpad},
+                                    {128, dpad > 96 ? 32 : 64, 4, dpad}};
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return FA_ELAUNCH;
+    }
+    fa_status result = FA_EUNSUPPORTED;
+    fa::TileConfig best{};
+    float best_ms = 0.0f;
+    for (const fa::TileConfig& c : cand) {
+        // one untimed launch; it also rejects configurations with no kernel for these inputs
+        st = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
+                         stream, &c);
+        if (st == FA_EUNSUPPORTED) continue;
+        if (st != FA_OK) {
+            result = st;
+            break;
+        }
+        bool ok = hipEventRecord(e0, s) == hipSuccess;
+        for (int r = 0; ok && r < reps; ++r)
+            ok = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
+                             stream, &c) == FA_OK;
+        ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
+        float ms = 0.0f;
+        ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        if (!ok) {
+            result = FA_ELAUNCH;
+            break;
+        }
+        if (result != FA_OK || ms < best_ms) {
+            best = c;
+            best_ms = ms;
+            result = FA_OK;
+        }
+    }
+    if (result == FA_OK) {
+        // o and lse end up holding the chosen configuration's result
+        result = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal,
+                             dtype, stream, &best);
+    }
+    int dev = 0;
+    if (result == FA_OK && hipGetDevice(&dev) != hipSuccess) result = FA_ELAUNCH;
+    if (result == FA_OK) {
+        fa::tuned_store(fa::TuneKey{dev, (int)dtype, causal ? 1 : 0, B, H, Nq, Nk, d}, best);
+        if (Br) *Br = best.br;
+        if (Bc) *Bc = best.bc;
+        if (waves) *waves = best.waves;
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return result;
+}
+
+void fa_tune_clear(void) {
+    std::lock_guard<std::mutex> lk(fa::g_tune_mu);
+    fa::g_tune_used = 0;
+    fa::g_tune_next = 0;
+    fa::g_tune_count.store(0, std::memory_order_release);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -132,6 +132,54 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
+ * fa_fwd_config -- fa_fwd with the tile configuration given instead of chosen.
+ *
+ * Br, Bc, waves: query rows per workgroup, keys per K/V tile and waves per workgroup, as
+ * fa_select_config and fa_tune_fwd report them. The kernels that exist: for fp16/bf16,
+ * (256, 64, 8) when every buffer is 16-byte aligned, d % 8 == 0 and d <= 128; (128, 64, 4);
+ * (64, 64, 4) when non-causal and d <= 96. For fp32, (128, 64, 4) for d <= 96 and
+ * (128, 32, 4) above. Any other triple returns FA_EUNSUPPORTED before any HIP call.
+ * Everything else (arguments, ownership, errors) is as for fa_fwd; the result is the same
+ * up to the order of the fp32 sums.
+ */
+fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        float scale, int causal, fa_dtype dtype, int Br, int Bc, int waves,
+                        void* stream);
+
+/*
+ * fa_tune_fwd -- measure every tile configuration that exists for this problem and keep
+ * the fastest.
+ *
+ * The pages' kernels pick tile sizes by hand and by search (page "Flash Attention Shared
+ * Memory constraint", the group-size search; page "Add Fused Multi-Head Attention example":
+ * its Python counterpart searches a space of hand-picked configurations). Here each
+ * configuration fa_fwd_config accepts
+ * runs once untimed and then `reps` times (1..1000) between two HIP events on `stream`;
+ * the fastest is written to *Br, *Bc, *waves (each may be NULL) and remembered for this
+ * exact problem (current device, dtype, B, H, Nq, Nk, d, causal). Later fa_fwd calls on the
+ * same problem launch it instead of the built-in choice, as long as the buffers allow it
+ * (a ping-pong choice needs 16-byte aligned buffers). The record holds up to 256 problems;
+ * beyond that the oldest is replaced.
+ *
+ * q, k, v, o, lse, sizes, scale, causal, dtype, stream: as for fa_fwd. On FA_OK, o and lse
+ * hold the result of the chosen configuration.
+ *
+ * Unlike fa_fwd this call blocks: it waits for the timed launches to finish. It creates
+ * two HIP events for its own duration and allocates no device memory.
+ *
+ * Errors: as fa_fwd, plus FA_EINVAL for reps outside 1..1000. FA_ELAUNCH if a launch or
+ * an event call fails; the record is then unchanged.
+ */
+fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      float scale, int causal, fa_dtype dtype, int reps, void* stream,
+                      int* Br, int* Bc, int* waves);
+
+/* Forgets every configuration fa_tune_fwd recorded (all devices). */
+void fa_tune_clear(void);
+
+/*
  * fa_bwd -- gradients of the attention forward, asynchronous on `stream`.
  *
  * Given the forward's inputs q, k, v, its outputs o and lse (as fa_fwd wrote them, same

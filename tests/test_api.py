@@ -28,8 +28,8 @@ def header_functions():
 
 def test_header_symbols_are_exported(L):
     names = header_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_status_str", "fa_select_config",
-                          "fa_version"}
+    assert set(names) == {"fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear",
+                          "fa_bwd", "fa_status_str", "fa_select_config", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
     assert set(fa.EXPORTED) == set(names)
@@ -90,6 +90,53 @@ def test_varlen_invalid_arguments(L, kw):
 @pytest.mark.parametrize("kw", [dict(d=257), dict(d=129, dtype=0), dict(Tq=2**26, mq=2**26, d=64)])
 def test_varlen_unsupported(L, kw):
     assert call_varlen(L, **kw) == fa.FA_EUNSUPPORTED
+
+
+def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0.125):
+    Br, Bc, waves = cfg
+    return L.fa_fwd_config(q, P, P, P, P, B, H, Nq, Nk, d, ctypes.c_float(scale), causal, dtype,
+                           Br, Bc, waves, None)
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    ((256, 64, 8), dict(dtype=0)),             # no fp32 ping-pong kernel
+    ((128, 64, 4), dict(dtype=0, d=128)),      # fp32 d > 96 uses 32-key tiles
+    ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys
+    ((64, 64, 4), dict(causal=1)),             # the key split is non-causal only
+    ((64, 64, 4), dict(d=128)),                # and d <= 96 only
+    ((256, 64, 8), dict(d=136)),               # ping-pong only up to d = 128
+    ((256, 64, 8), dict(d=60)),                # and for d % 8 == 0
+    ((256, 64, 8), dict(q=P + 2)),             # and for 16-byte aligned rows
+    ((512, 64, 16), dict()), ((128, 64, 8), dict()), ((0, 0, 0), dict()),
+])
+def test_fwd_config_unsupported(L, cfg, kw):
+    """Configurations with no kernel are rejected before any HIP call."""
+    assert call_cfg(L, cfg, **kw) == fa.FA_EUNSUPPORTED
+
+
+def test_fwd_config_invalid_arguments(L):
+    assert call_cfg(L, (128, 64, 4), B=0) == fa.FA_EINVAL
+    assert call_cfg(L, (128, 64, 4), q=None) == fa.FA_EINVAL
+    assert call_cfg(L, (128, 64, 4), scale=float("nan")) == fa.FA_EINVAL
+
+
+def call_tune(L, reps=5, q=P, B=1, d=64, scale=0.125):
+    out = [ctypes.c_int(-1) for _ in range(3)]
+    rc = L.fa_tune_fwd(q, P, P, P, P, B, 1, 8, 8, d, ctypes.c_float(scale), 0, 2, reps, None,
+                       *[ctypes.byref(x) for x in out])
+    return rc, [x.value for x in out]
+
+
+@pytest.mark.parametrize("kw", [dict(reps=0), dict(reps=1001), dict(q=None), dict(B=0), dict(d=0),
+                                dict(scale=float("inf"))])
+def test_tune_invalid_arguments(L, kw):
+    rc, out = call_tune(L, **kw)
+    assert rc == fa.FA_EINVAL and out == [-1, -1, -1]
+
+
+def test_tune_clear_needs_no_gpu(L):
+    fa.fa_tune_clear()
+    fa.fa_tune_clear()
 
 
 def call_bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, delta=P, B=1, H=1, Nq=8, Nk=8, d=64,

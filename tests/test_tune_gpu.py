@@ -1,0 +1,130 @@
+"""GPU checks of the tile-configuration entry points: every kernel a problem admits (forced
+through fa_fwd_config) against the fp64 oracle on the same inputs, and fa_tune_fwd's record
+steering later fa_fwd calls.
+
+Tolerances as for the forward: O max-abs <= 1e-4 (fp32) and <= 2e-2 (fp16/bf16), L <= 1e-3.
+The kernels are deterministic (no atomics), so "fa_fwd launched configuration X" is checked
+as bit-equality with fa_fwd_config(X) on the same inputs.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_58_amd as fa
+import oracle
+from exact_attention_58_amd.workloads import make_random
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+TOL_L = 1e-3
+ALL = [{"Br": 256, "Bc": 64, "waves": 8}, {"Br": 128, "Bc": 64, "waves": 4},
+       {"Br": 64, "Bc": 64, "waves": 4}, {"Br": 128, "Bc": 32, "waves": 4}]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.ensure_built()
+    fa.lib()
+    fa.fa_tune_clear()
+    yield
+    fa.fa_tune_clear()
+
+
+def admitted(dt, d, causal):
+    """The configurations fa_fwd_config accepts for contiguous (16-byte aligned) tensors."""
+    dpad = (d + 31) // 32 * 32
+    if dt == "f32":
+        return [{"Br": 128, "Bc": 32 if dpad > 96 else 64, "waves": 4}]
+    out = [{"Br": 128, "Bc": 64, "waves": 4}]
+    if d % 8 == 0 and dpad <= 128:
+        out.append({"Br": 256, "Bc": 64, "waves": 8})
+    if not causal and dpad <= 96:
+        out.append({"Br": 64, "Bc": 64, "waves": 4})
+    return out
+
+
+def inputs(dt, B, H, Nq, Nk, d, seed):
+    q = make_random((B, H, Nq, d), dt, seed)
+    k = make_random((B, H, Nk, d), dt, seed + 1)
+    v = make_random((B, H, Nk, d), dt, seed + 2)
+    return q, k, v
+
+
+CASES = [
+    ("bf16", 1, 2, 300, 700, 64, False), ("bf16", 1, 2, 300, 700, 64, True),
+    ("f16", 2, 2, 257, 513, 128, False), ("f16", 1, 2, 129, 1000, 96, False),
+    ("bf16", 1, 1, 200, 200, 200, True), ("bf16", 1, 2, 100, 90, 40, False),
+    ("f32", 1, 2, 300, 700, 64, False), ("f32", 1, 1, 100, 300, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_every_admitted_config_matches_oracle(case):
+    dt, B, H, Nq, Nk, d, causal = case
+    q, k, v = inputs(dt, B, H, Nq, Nk, d, 300 + Nq + d)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), scale, causal)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ok = admitted(dt, d, causal)
+    for cfg in ALL:
+        o = torch.empty_like(qd)
+        lse = torch.empty(qd.shape[:-1], dtype=torch.float32, device="cuda")
+        if cfg not in ok:
+            with pytest.raises(fa.FaError) as e:
+                fa.fa_fwd_config(qd, kd, vd, o, lse, scale, causal, cfg)
+            assert e.value.status == fa.FA_EUNSUPPORTED
+            continue
+        fa.fa_fwd_config(qd, kd, vd, o, lse, scale, causal, cfg)
+        torch.cuda.synchronize()
+        oe = float(np.max(np.abs(o.double().cpu().numpy() - o_ref)))
+        le = float(np.max(np.abs(lse.double().cpu().numpy() - l_ref)))
+        say(f"  {case} {cfg}: max|dO| {oe:.3e} max|dL| {le:.3e}")
+        assert oe <= TOL_O[dt] and le <= TOL_L, (case, cfg)
+
+
+@pytest.mark.parametrize("case", [("bf16", 2, 4, 1000, 3001, 64, False), ("f16", 1, 8, 700, 700, 128, True),
+                                  ("bf16", 1, 2, 300, 700, 96, False)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_tune_record_steers_fa_fwd(case):
+    dt, B, H, Nq, Nk, d, causal = case
+    q, k, v = (t.cuda() for t in inputs(dt, B, H, Nq, Nk, d, 500 + d))
+    scale = 1.0 / math.sqrt(d)
+    fa.fa_tune_clear()
+    rule = fa.fa_select_config(dt, B, H, Nq, Nk, d, causal, num_cus=torch.cuda.get_device_properties(0).multi_processor_count)
+    rule = {k_: rule[k_] for k_ in ("Br", "Bc", "waves")}
+
+    def run(cfg=None):
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+        if cfg is None:
+            fa.fa_fwd(q, k, v, o, lse, scale, causal)
+        else:
+            fa.fa_fwd_config(q, k, v, o, lse, scale, causal, cfg)
+        torch.cuda.synchronize()
+        return o, lse
+
+    o0, l0 = run()
+    o_r, l_r = run(rule)
+    assert torch.equal(o0, o_r) and torch.equal(l0, l_r)  # untuned: the built-in choice
+    ot = torch.empty_like(q)
+    lt = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    best = fa.fa_tune_fwd(q, k, v, ot, lt, scale, causal, reps=3)
+    say(f"  {case}: built-in {rule}, tuned {best}")
+    assert best in admitted(dt, d, causal)
+    o1, l1 = run()
+    o_b, l_b = run(best)
+    assert torch.equal(o1, o_b) and torch.equal(l1, l_b)    # tuned: the recorded choice
+    assert torch.equal(ot, o_b) and torch.equal(lt, l_b)    # the tuning call's own output
+    fa.fa_tune_clear()
+    o2, l2 = run()
+    assert torch.equal(o2, o_r) and torch.equal(l2, l_r)    # cleared: built-in again
