@@ -95,8 +95,12 @@ __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* t
 
 // ---------------------------------------------------------------- dK, dV
 
+// Up to d = 96 two waves share a SIMD (the registers fit; one wave's LDS reads and staged
+// loads overlap the other's products, about 1.5x the throughput of one wave per SIMD); at
+// d = 128 the accumulators and resident K, V fragments need one wave per SIMD.
 template <typename T, int DP, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DP <= 96 ? 2 : 1, DP <= 96 ? 2 : 1)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     constexpr int BK = 128, BQ = 64;  // keys per workgroup, queries per tile
     constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
@@ -235,7 +239,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 // ---------------------------------------------------------------- dQ
 
 template <typename T, int DP, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DP <= 96 ? 2 : 1, DP <= 96 ? 2 : 1)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     constexpr int BR = 128, BC = 64;  // queries per workgroup, keys per tile
     constexpr int STR = DP + 8;
