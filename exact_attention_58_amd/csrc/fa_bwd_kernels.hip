@@ -95,13 +95,16 @@ __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* t
 
 // ---------------------------------------------------------------- dK, dV
 
-// Up to d = 96 two waves share a SIMD (the registers fit; one wave's LDS reads and staged
-// loads overlap the other's products, about 1.5x the throughput of one wave per SIMD); at
-// d = 128 the accumulators and resident K, V fragments need one wave per SIMD.
-template <typename T, int DP, bool CAUSAL>
+// MODE 0 computes dK and dV together; MODE 1 only dV (S, P, P^T dO) and MODE 2 only dK
+// (S, dP, dS, dS^T Q), which recompute S each but hold half the accumulators. Two waves
+// share a SIMD whenever the registers fit (up to d = 96 for MODE 0, every d for the single
+// modes): one wave's LDS reads and staged loads then overlap the other's products, about
+// 1.5x the throughput of one wave per SIMD.
+template <typename T, int DP, bool CAUSAL, int MODE>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DP <= 96 ? 2 : 1, DP <= 96 ? 2 : 1)))
+                          amdgpu_waves_per_eu(DP <= 96 || MODE != 0 ? 2 : 1, DP <= 96 || MODE != 0 ? 2 : 1)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
+    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
     constexpr int BK = 128, BQ = 64;  // keys per workgroup, queries per tile
     constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
     constexpr int NDS = DP / 16, NDB = DP / 32;
@@ -132,7 +135,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
         kf[ds] = load_chunk16<true>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
-        vf[ds] = load_chunk16<true>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
+        if constexpr (DO_DK) vf[ds] = load_chunk16<true>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
     }
 
     f32x16 dva[NDB], dka[NDB];
@@ -178,7 +181,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
                 s = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], s);
-                dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+                if constexpr (DO_DK) dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
             }
             // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey
             unsigned ppk[8], spk[8];
@@ -186,7 +189,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
             for (int g = 0; g < 4; ++g) {
                 const int ql = qb * 32 + 8 * g + 4 * h32;
                 const f32x4 lv = *(const f32x4*)(Ls + ql);
-                const f32x4 dv = *(const f32x4*)(Ds + ql);
+                f32x4 dv = {};
+                if constexpr (DO_DK) dv = *(const f32x4*)(Ds + ql);
                 float pv[4], sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -194,12 +198,16 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                     const bool ok = mykey < Nk && q < Nq && (!CAUSAL || mykey <= q);
                     const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
                     pv[e] = p;
-                    sv[e] = p * (dp[4 * g + e] - dv[e]);
+                    if constexpr (DO_DK) sv[e] = p * (dp[4 * g + e] - dv[e]);
                 }
-                ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
-                ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
-                spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
-                spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
+                if constexpr (DO_DV) {
+                    ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                    ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                }
+                if constexpr (DO_DK) {
+                    spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
+                    spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
+                }
             }
             // dV += P^T dO and dK += dS^T Q over the two 16-query steps of this block
 #pragma unroll
@@ -208,10 +216,14 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                 const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
-                    const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
-                    dva[db] = Half<T>::mfma(pa, gb, dva[db]);
-                    dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
+                    if constexpr (DO_DV) {
+                        const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
+                        dva[db] = Half<T>::mfma(pa, gb, dva[db]);
+                    }
+                    if constexpr (DO_DK) {
+                        const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
+                        dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
+                    }
                 }
             }
         }
@@ -229,8 +241,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
         for (int r = 0; r < 16; ++r) {
             const int key = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
             if (key < Nk) {
-                dvg[(int64_t)key * d + col] = Half<T>::one(dva[db][r]);
-                dkg[(int64_t)key * d + col] = Half<T>::one(dka[db][r] * sc);
+                if constexpr (DO_DV) dvg[(int64_t)key * d + col] = Half<T>::one(dva[db][r]);
+                if constexpr (DO_DK) dkg[(int64_t)key * d + col] = Half<T>::one(dka[db][r] * sc);
             }
         }
     }
@@ -238,9 +250,9 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 
 // ---------------------------------------------------------------- dQ
 
+// Two waves per SIMD at every head dim (the registers fit 256 per wave).
 template <typename T, int DP, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DP <= 96 ? 2 : 1, DP <= 96 ? 2 : 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     constexpr int BR = 128, BC = 64;  // queries per workgroup, keys per tile
     constexpr int STR = DP + 8;
@@ -362,10 +374,21 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return (int)e;
     const int n_kt = (a.Nk + 127) / 128;
     const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
-    if (a.causal)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true>), dim3(g1), dim3(256), 0, st, a, n_kt);
-    else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false>), dim3(g1), dim3(256), 0, st, a, n_kt);
+    if constexpr (DP <= 96) {
+        if (a.causal)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 0>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 0>), dim3(g1), dim3(256), 0, st, a, n_kt);
+    } else {
+        // dV and dK as two kernels that each fit two waves per SIMD
+        if (a.causal) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 1>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 2>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        } else {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 1>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 2>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        }
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     const int n_qt = (a.Nq + 127) / 128;
