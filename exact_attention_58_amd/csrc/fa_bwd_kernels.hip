@@ -32,27 +32,28 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
 
-// Row terms: delta[r] = sum_c dO[r][c] O[r][c] for every flat query row r (d % 8 == 0).
+// Row terms: delta[r] = sum_c dO[r][c] O[r][c] for every flat query row r (d % 8 == 0, d <= 128).
+// Sixteen lanes share a row, one 16-byte chunk each, so a wave reads four whole rows of O and
+// of dO per instruction (coalesced); the sixteen partial sums meet through lane shuffles.
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, float* delta, int64_t rows, int d) {
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= rows) return;
-    const uint16_t* op = o + r * d;
-    const uint16_t* gp = dout + r * d;
+    const int sub = threadIdx.x & 15;
+    const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     float acc = 0.0f;
-    for (int c = 0; c < d; c += 8) {
-        const u32x4 a = *(const u32x4*)(op + c);
-        const u32x4 b = *(const u32x4*)(gp + c);
+    if (r < rows && sub * 8 < d) {
+        const u32x4 a = *(const u32x4*)(o + r * d + sub * 8);
+        const u32x4 b = *(const u32x4*)(dout + r * d + sub * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float a0 = Half<T>::lo(a[i]), a1 = Half<T>::hi(a[i]);
-            const float b0 = Half<T>::lo(b[i]), b1 = Half<T>::hi(b[i]);
-            acc = __builtin_fmaf(a0, b0, acc);
-            acc = __builtin_fmaf(a1, b1, acc);
+            acc = __builtin_fmaf(Half<T>::lo(a[i]), Half<T>::lo(b[i]), acc);
+            acc = __builtin_fmaf(Half<T>::hi(a[i]), Half<T>::hi(b[i]), acc);
         }
     }
-    delta[r] = acc;
+    // every lane takes part in the shuffles, also past the last row
+#pragma unroll
+    for (int m = 8; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 16);
+    if (r < rows && sub == 0) delta[r] = acc;
 }
 
 // Tile of 64 rows x DP columns (16-bit) staged through registers into LDS rows of STR
@@ -368,7 +369,9 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 template <typename T, int DP>
 int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.H * a.Nq;
-    hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st,
+    static_assert(DP <= 128, "row terms: at most 16 chunks of 8 per row");
+    if ((rows + 15) / 16 > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, a.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
