@@ -71,6 +71,11 @@ __device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a
 // longest sequences; there pair p goes to XCD p % 8 with all its query tiles, which spreads
 // every sequence's heads over all XCDs (a bijection when the pair count is a multiple of 8,
 // otherwise the dense order is kept).
+// Causal dense grids give query tile t of every pair the same work, and the kernels run
+// tiles heaviest first (they reverse qt). Within an XCD the pair-major order would start the
+// heaviest tiles of its last pairs only after the lighter tiles of its first pairs; when
+// every XCD owns whole pairs ((B*H) % 8 == 0) an XCD's workgroups instead go tile-major
+// over its pairs, so all its heavy tiles start first (longest-job-first dispatch).
 struct TileId {
     int bh, qt;
 };
@@ -79,6 +84,12 @@ __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a
     if (a.cu_q != nullptr && (a.B * a.H) % 8 == 0) {
         const int k = i >> 3, m = k / n_qtiles;
         return {(i & 7) + 8 * m, k - m * n_qtiles};
+    }
+    if (a.cu_q == nullptr && a.causal && (a.B * a.H) % 8 == 0) {
+        const int pairs = (a.B * a.H) >> 3;        // pairs per XCD
+        const int x = i & 7, slot = i >> 3;       // XCD, position in its dispatch order
+        const int qt = slot / pairs;
+        return {x * pairs + (slot - qt * pairs), qt};
     }
     const int wg = xcd_remap(i, gridDim.x);
     const int bh = wg / n_qtiles;
