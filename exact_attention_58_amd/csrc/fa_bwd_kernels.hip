@@ -116,9 +116,9 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / n_ktiles;
-    const int kt = wg - bh * n_ktiles;
+    // causal: key tile 0 sees every query tile, the heaviest; tile-major dispatch per XCD
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL);
+    const int bh = pt.pair, kt = pt.tile;
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int k0 = kt * BK;
     const int kw0 = k0 + 32 * wave;
@@ -263,10 +263,10 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / n_qtiles;
-    int qt = wg - bh * n_qtiles;
-    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL);
+    const int bh = pt.pair;
+    int qt = pt.tile;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first (tile-major dispatch per XCD)
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int q0 = qt * BR;
     const int r0w = q0 + 32 * wave;

@@ -30,6 +30,29 @@ __device__ inline int xcd_remap(int bid, int total) {
     return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Workgroup bid of a grid of n_pairs x n_tiles workgroups -> (pair, tile), every XCD owning
+// a contiguous run of pairs (workgroups are dealt to the XCDs in turn). Pair-major inside an
+// XCD by default: consecutive workgroups share one pair's K and V in the XCD's L2. With
+// tile_major, and when the pairs split evenly over the XCDs, the XCD's workgroups go
+// tile-major over its pairs instead: in causal grids tile t has the same work in every pair,
+// so when tile 0 is the heaviest all of the XCD's heavy tiles are dispatched first
+// (longest job first) rather than after the light tiles of its first pairs.
+struct PairTile {
+    int pair, tile;
+};
+__device__ inline PairTile xcd_pair_tile(int bid, int total, int n_tiles, int n_pairs, bool tile_major) {
+    constexpr int kXcds = 8;
+    if (tile_major && n_pairs % kXcds == 0) {
+        const int per = n_pairs / kXcds;
+        const int x = bid % kXcds, slot = bid / kXcds;
+        const int t = slot / per;
+        return {x * per + (slot - t * per), t};
+    }
+    const int wg = xcd_remap(bid, total);
+    const int p = wg / n_tiles;
+    return {p, wg - p * n_tiles};
+}
+
 __device__ inline float wave_half_max(float x) {
     u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));

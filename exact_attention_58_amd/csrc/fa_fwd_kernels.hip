@@ -72,10 +72,8 @@ __device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a
 // every sequence's heads over all XCDs (a bijection when the pair count is a multiple of 8,
 // otherwise the dense order is kept).
 // Causal dense grids give query tile t of every pair the same work, and the kernels run
-// tiles heaviest first (they reverse qt). Within an XCD the pair-major order would start the
-// heaviest tiles of its last pairs only after the lighter tiles of its first pairs; when
-// every XCD owns whole pairs ((B*H) % 8 == 0) an XCD's workgroups instead go tile-major
-// over its pairs, so all its heavy tiles start first (longest-job-first dispatch).
+// tiles heaviest first (they reverse qt), so they take the XCD-local tile-major order
+// (xcd_pair_tile): all heavy tiles of an XCD's pairs start before the light ones.
 struct TileId {
     int bh, qt;
 };
@@ -85,15 +83,8 @@ __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a
         const int k = i >> 3, m = k / n_qtiles;
         return {(i & 7) + 8 * m, k - m * n_qtiles};
     }
-    if (a.cu_q == nullptr && a.causal && (a.B * a.H) % 8 == 0) {
-        const int pairs = (a.B * a.H) >> 3;        // pairs per XCD
-        const int x = i & 7, slot = i >> 3;       // XCD, position in its dispatch order
-        const int qt = slot / pairs;
-        return {x * pairs + (slot - qt * pairs), qt};
-    }
-    const int wg = xcd_remap(i, gridDim.x);
-    const int bh = wg / n_qtiles;
-    return {bh, wg - bh * n_qtiles};
+    const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.cu_q == nullptr && a.causal);
+    return {pt.pair, pt.tile};
 }
 
 // Query rows [r0, r0 + br) of a sequence that has queries but no keys: the softmax sum is
