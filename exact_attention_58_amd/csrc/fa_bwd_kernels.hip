@@ -31,6 +31,8 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
+// workgroups an XCD holds at once: 32 CUs x two 4-wave workgroups (two waves per SIMD)
+constexpr int kXcdSlots = 64;
 
 // Row terms: delta[r] = sum_c dO[r][c] O[r][c] for every flat query row r (d % 8 == 0, d <= 128).
 // Sixteen lanes share a row, one 16-byte chunk each, so a wave reads four whole rows of O and
@@ -117,7 +119,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
     // causal: key tile 0 sees every query tile, the heaviest; tile-major dispatch per XCD
-    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL);
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, kXcdSlots);
     const int bh = pt.pair, kt = pt.tile;
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int k0 = kt * BK;
@@ -263,7 +265,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
-    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL);
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL, kXcdSlots);
     const int bh = pt.pair;
     int qt = pt.tile;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first (tile-major dispatch per XCD)

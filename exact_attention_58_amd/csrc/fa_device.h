@@ -33,20 +33,31 @@ __device__ inline int xcd_remap(int bid, int total) {
 // Workgroup bid of a grid of n_pairs x n_tiles workgroups -> (pair, tile), every XCD owning
 // a contiguous run of pairs (workgroups are dealt to the XCDs in turn). Pair-major inside an
 // XCD by default: consecutive workgroups share one pair's K and V in the XCD's L2. With
-// tile_major, and when the pairs split evenly over the XCDs, the XCD's workgroups go
-// tile-major over its pairs instead: in causal grids tile t has the same work in every pair,
-// so when tile 0 is the heaviest all of the XCD's heavy tiles are dispatched first
-// (longest job first) rather than after the light tiles of its first pairs.
+// tile_major, and when the pairs split evenly over the XCDs, the XCD's pairs go in groups of
+// G, tile-major inside a group: in causal grids tile t has the same work in every pair, so
+// when tile 0 is the heaviest the heavy tiles of a group start together and the next
+// group's heavy tiles fill in behind the light ones (longest job first), where pair-major
+// order would start the heavy tiles of the XCD's last pairs after everything else. G is the
+// smallest group whose tiles fill the `slots` workgroups an XCD holds at once; a larger G
+// balances no better and only spreads the XCD's L2 over more pairs' K and V. The last group
+// may be smaller.
 struct PairTile {
     int pair, tile;
 };
-__device__ inline PairTile xcd_pair_tile(int bid, int total, int n_tiles, int n_pairs, bool tile_major) {
+__device__ inline PairTile xcd_pair_tile(int bid, int total, int n_tiles, int n_pairs, bool tile_major,
+                                         int slots) {
     constexpr int kXcds = 8;
     if (tile_major && n_pairs % kXcds == 0) {
         const int per = n_pairs / kXcds;
         const int x = bid % kXcds, slot = bid / kXcds;
-        const int t = slot / per;
-        return {x * per + (slot - t * per), t};
+        const int g = min(per, (slots + n_tiles - 1) / n_tiles);
+        const int full = per / g;                 // groups of g pairs
+        int grp = slot / (g * n_tiles);
+        const int gs = grp < full ? g : per - full * g;  // pairs in this group
+        grp = min(grp, full);
+        const int r = slot - grp * g * n_tiles;
+        const int t = r / gs;
+        return {x * per + grp * g + (r - t * gs), t};
     }
     const int wg = xcd_remap(bid, total);
     const int p = wg / n_tiles;

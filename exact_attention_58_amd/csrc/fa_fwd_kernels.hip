@@ -77,13 +77,14 @@ __device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a
 struct TileId {
     int bh, qt;
 };
-__device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles) {
+// slots: workgroups of the calling kernel an XCD holds at once (32 CUs x workgroups per CU).
+__device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles, int slots) {
     const int i = blockIdx.x;
     if (a.cu_q != nullptr && (a.B * a.H) % 8 == 0) {
         const int k = i >> 3, m = k / n_qtiles;
         return {(i & 7) + 8 * m, k - m * n_qtiles};
     }
-    const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.cu_q == nullptr && a.causal);
+    const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.cu_q == nullptr && a.causal, slots);
     return {pt.pair, pt.tile};
 }
 
@@ -249,7 +250,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
-    const TileId wt = tile_of(a, n_qtiles);
+    const TileId wt = tile_of(a, n_qtiles, DP > 128 ? 32 : 64);
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
@@ -472,7 +473,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int grp = wave / WPG, wig = wave % WPG;
 
-    const TileId wt = tile_of(a, n_qtiles);
+    const TileId wt = tile_of(a, n_qtiles, 32);
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
@@ -763,7 +764,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
 
-    const TileId wt = tile_of(a, n_qtiles);
+    const TileId wt = tile_of(a, n_qtiles, 64);
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
