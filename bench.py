@@ -27,19 +27,23 @@ sys.path.insert(0, ROOT)
 # MI355X published dense peaks (no sparsity), TFLOP/s, and HBM3E bandwidth, GB/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_58_amd", "csrc", "fa_fwd_kernels.hip")
+# the forward kernels' source: the kernel file and the device headers it includes
+KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
+              for f in ("fa_fwd_kernels.hip", "fa_device.h", "fa_internal.h")]
 
 # HBM traffic per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (KiB per
 # dispatch, scaled by the factor a plain copy kernel of known size reads on the same
 # counters), keyed by workload, valid only for the kernel source whose sha256 prefix is
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
-    # profiles/fwd32_pages_f32.txt: FETCH_SIZE 24654 KiB x 2.0 + WRITE_SIZE 16640 KiB x 1.0
-    "pages_f32": {"bytes": 67530688, "kernel_sha": "b4c8f54041b8a009"},
-    # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE 98406.8 KiB x 2.0 + WRITE_SIZE 66560 KiB x 1.0
-    "d128_bf16": {"bytes": 269694549, "kernel_sha": "b4c8f54041b8a009"},
-    # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE 29775.4 KiB x 2.0 + WRITE_SIZE 16896 KiB x 1.0
-    "long_causal_bf16": {"bytes": 78281472, "kernel_sha": "b4c8f54041b8a009"},
+    # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+    "pages_f32": {"bytes": 67510878, "kernel_sha": "2547ac2464df1474"},
+    # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+    "d128_bf16": {"bytes": 269685294, "kernel_sha": "2547ac2464df1474"},
+    # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+    "d128_bf16_causal": {"bytes": 304465166, "kernel_sha": "2547ac2464df1474"},
+    # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
+    "long_causal_bf16": {"bytes": 78283162, "kernel_sha": "2547ac2464df1474"},
 }
 
 
@@ -48,8 +52,11 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def time_workload(fa, torch, w, steps, warmup, inputs=None):
