@@ -71,20 +71,24 @@ __device__ __attribute__((always_inline)) inline Slice slice_of(const FwdArgs& a
 // longest sequences; there pair p goes to XCD p % 8 with all its query tiles, which spreads
 // every sequence's heads over all XCDs (a bijection when the pair count is a multiple of 8,
 // otherwise the dense order is kept).
-// Causal dense grids give query tile t of every pair the same work, and the kernels run
-// tiles heaviest first (they reverse qt), so they take the XCD-local tile-major order
-// (xcd_pair_tile): all heavy tiles of an XCD's pairs start before the light ones.
+// Causal grids run tiles heaviest first (the kernels reverse qt) and take the XCD-local
+// grouped tile-major order of xcd_pair_tile, so the heavy tiles of an XCD's pairs start
+// before the light ones. Dense pairs all have equal work; packed sequences differ in
+// length, and tile-major order over their pairs still starts the longest sequences' last
+// query tiles first (simulated with the bench's packed lengths: 220 -> 212 tile-units per
+// XCD against an ideal of 204).
 struct TileId {
     int bh, qt;
 };
 // slots: workgroups of the calling kernel an XCD holds at once (32 CUs x workgroups per CU).
 __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles, int slots) {
     const int i = blockIdx.x;
+    const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.causal, slots);
     if (a.cu_q != nullptr && (a.B * a.H) % 8 == 0) {
-        const int k = i >> 3, m = k / n_qtiles;
-        return {(i & 7) + 8 * m, k - m * n_qtiles};
+        // XCD x takes pairs x, x + 8, x + 16, ...: its m-th pair is the m-th of its run above
+        const int x = i & 7;
+        return {x + 8 * (pt.pair - x * ((a.B * a.H) >> 3)), pt.tile};
     }
-    const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.cu_q == nullptr && a.causal, slots);
     return {pt.pair, pt.tile};
 }
 
