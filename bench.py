@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67510878, "kernel_sha": "2547ac2464df1474"},
+    "pages_f32": {"bytes": 67516169, "kernel_sha": "af115e29e8bb1467"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269685294, "kernel_sha": "2547ac2464df1474"},
+    "d128_bf16": {"bytes": 269684345, "kernel_sha": "af115e29e8bb1467"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 304465166, "kernel_sha": "2547ac2464df1474"},
+    "d128_bf16_causal": {"bytes": 322075044, "kernel_sha": "af115e29e8bb1467"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78283162, "kernel_sha": "2547ac2464df1474"},
+    "long_causal_bf16": {"bytes": 78314775, "kernel_sha": "af115e29e8bb1467"},
 }
 
 
