@@ -186,7 +186,12 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                 s = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], s);
                 if constexpr (DO_DK) dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
             }
-            // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey
+            // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey. The weight is
+            // kept iff off = 8 (r/4) + r%4 >= lo: lo puts the causal diagonal (q >= mykey) in
+            // one compare per register and masks every query of a key past Nk. Padded query
+            // rows (q >= Nq) need no test: their Q, dO, L and D are zero, so the weight
+            // exp2(0) = 1 meets dO = 0 and dP - D = 0 and adds nothing.
+            const int lo = mykey >= Nk ? 64 : CAUSAL ? mykey - q0 - qb * 32 - 4 * h32 : -64;
             unsigned ppk[8], spk[8];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -197,9 +202,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                 float pv[4], sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int q = q0 + ql + e;
-                    const bool ok = mykey < Nk && q < Nq && (!CAUSAL || mykey <= q);
-                    const float p = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
+                    const float p = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
                     pv[e] = p;
                     if constexpr (DO_DK) sv[e] = p * (dp[4 * g + e] - dv[e]);
                 }
