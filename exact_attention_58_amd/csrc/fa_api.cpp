@@ -132,12 +132,17 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // loads, its grid still gives every compute unit a workgroup and the key loop is
         // long enough for its pipeline to pay off. Short key sequences (<= 512, HBM-bound)
         // go to the 4-wave kernel, whose smaller workgroups overlap their loads better
-        // (bf16 d=128, N=128: 4.7 vs 2.8 TB/s on MI355X).
+        // (bf16 d=128, N=128: 4.7 vs 2.8 TB/s on MI355X). Causal grids keep the 4-wave
+        // kernel longer: its 128-row tiles waste less on the diagonal and its shorter
+        // workgroups balance better. Measured crossover (bf16, MI355X): 2048 keys for
+        // d > 64 (d=128, N=1024: 628 vs 551 TFLOP/s; N=4096: 834 vs 914), 4096 keys for
+        // d <= 64 (N=3072: 587 vs 517; N=16384: 719 vs 793).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
+        const int64_t pp_min_keys = !causal ? 512 : d <= 64 ? 4096 : 2048;
         if (d > 128) {
             // head dims past 128: the 4-wave kernel, one wave per SIMD
-        } else if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > 512) {
+        } else if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > pp_min_keys) {
             c.waves = 8;
             c.br = 256;
         } else if (!causal && c.dpad <= 96 && wgs128 < num_cus && Nk > 2 * c.bc) {

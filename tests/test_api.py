@@ -226,6 +226,12 @@ def test_select_config_grid_fill(dtype):
     assert edge["waves"] == 4
     longer = fa.fa_select_config(dtype, 8, 128, 1024, 513, 128, False, num_cus=256)
     assert longer["waves"] == 8
+    # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 4096 keys (d <= 64)
+    for d, last_4wave in ((128, 2048), (96, 2048), (64, 4096), (32, 4096)):
+        at = fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, True, num_cus=256)
+        past = fa.fa_select_config(dtype, 4, 32, last_4wave + 1, last_4wave + 1, d, True, num_cus=256)
+        assert at["waves"] == 4 and past["waves"] == 8, (d, at, past)
+        assert fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, False, num_cus=256)["waves"] == 8
 
 
 def test_select_config_errors():

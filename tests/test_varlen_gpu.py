@@ -93,8 +93,9 @@ def test_varlen_other_head_dims(dt, d):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_pingpong_kernel(causal):
-    """Long sequences on many heads: the 256-row ping-pong kernel (heads 0 and 15 checked)."""
-    lq = [1024, 700, 513, 1, 999, 256, 0, 800]
+    """Long sequences on many heads: the 256-row ping-pong kernel (heads 0 and 15 checked).
+    The longest sequence passes 2048 keys, where causal grids leave the 4-wave kernel."""
+    lq = [2400, 700, 513, 1, 999, 256, 0, 800]
     run_case("bf16", 16, lq, lq, 128, causal, seed=41, heads=[0, 15], expect_waves=8)
 
 
