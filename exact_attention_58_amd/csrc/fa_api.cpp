@@ -136,13 +136,16 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // kernel longer: its 128-row tiles waste less on the diagonal and its shorter
         // workgroups balance better. Measured crossover (bf16, MI355X): 2048 keys for
         // d > 64 (d=128, N=1024: 628 vs 551 TFLOP/s; N=4096: 834 vs 914), 4096 keys for
-        // d <= 64 (N=3072: 587 vs 517; N=16384: 719 vs 793).
+        // d <= 64 (N=3072: 587 vs 517; N=16384: 719 vs 793). Head dims up to 32 stay on the
+        // 4-wave kernel at every length: with four exp2 per MFMA both kernels are bound by
+        // the softmax's vector work, and the smaller workgroups do it faster (d=32, N=4096:
+        // 575 vs 515 TFLOP/s).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
         const int64_t pp_min_keys = !causal ? 512 : d <= 64 ? 4096 : 2048;
         if (d > 128) {
             // head dims past 128: the 4-wave kernel, one wave per SIMD
-        } else if (aligned && d % 8 == 0 && wgs256 >= num_cus && Nk > pp_min_keys) {
+        } else if (aligned && d % 8 == 0 && d > 32 && wgs256 >= num_cus && Nk > pp_min_keys) {
             c.waves = 8;
             c.br = 256;
         } else if (!causal && c.dpad <= 96 && wgs128 < num_cus && Nk > 2 * c.bc) {

@@ -226,8 +226,11 @@ def test_select_config_grid_fill(dtype):
     assert edge["waves"] == 4
     longer = fa.fa_select_config(dtype, 8, 128, 1024, 513, 128, False, num_cus=256)
     assert longer["waves"] == 8
+    # head dims up to 32: the 4-wave kernel at every length
+    for causal in (False, True):
+        assert fa.fa_select_config(dtype, 4, 16, 16384, 16384, 32, causal, num_cus=256)["waves"] == 4
     # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 4096 keys (d <= 64)
-    for d, last_4wave in ((128, 2048), (96, 2048), (64, 4096), (32, 4096)):
+    for d, last_4wave in ((128, 2048), (96, 2048), (64, 4096)):
         at = fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, True, num_cus=256)
         past = fa.fa_select_config(dtype, 4, 32, last_4wave + 1, last_4wave + 1, d, True, num_cus=256)
         assert at["waves"] == 4 and past["waves"] == 8, (d, at, past)
