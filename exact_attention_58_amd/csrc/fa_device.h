@@ -64,13 +64,15 @@ __device__ inline PairTile xcd_pair_tile(int bid, int total, int n_tiles, int n_
     return {p, wg - p * n_tiles};
 }
 
+// (NaN-propagating maximum / minimum: no canonicalising copies; equal to fmaxf / fminf on
+// scores and -inf)
 __device__ inline float wave_half_max(float x) {
     u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    return __builtin_elementwise_maximum(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ inline float wave_half_min(float x) {
     u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fminf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+    return __builtin_elementwise_minimum(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ inline float wave_half_sum(float x) {
     u32x2 s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

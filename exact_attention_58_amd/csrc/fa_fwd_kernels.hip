@@ -102,8 +102,10 @@ __device__ void write_empty_rows(const FwdArgs& a, const Slice& sl, int r0, int 
     for (int i = threadIdx.x; i < rows; i += blockDim.x) a.lse[sl.q0 + r0 + i] = kNegInf;
 }
 
-// Maximum of the NKB*16 values of s as a balanced tree (v_max3), so the dependency chain is
-// logarithmic in the number of values instead of linear. MIN selects the minimum instead.
+// Maximum of the NKB*16 values of s as a balanced tree (v_maximum3), so the dependency chain
+// is logarithmic in the number of values instead of linear. MIN selects the minimum instead.
+// The NaN-propagating maximum needs no canonicalising copies of the MFMA results, which the
+// IEEE maxnum (fmaxf) adds before each v_max; on scores and -inf the two agree.
 template <int NKB, bool MIN>
 __device__ __attribute__((always_inline)) inline float tile_extreme(const f32x16 (&s)[NKB]) {
     float v[NKB * 16];
@@ -121,7 +123,8 @@ __device__ __attribute__((always_inline)) inline float tile_extreme(const f32x16
             const float a = v[3 * i];
             const float b = 3 * i + 1 < n ? v[3 * i + 1] : a;
             const float c = 3 * i + 2 < n ? v[3 * i + 2] : a;
-            v[i] = MIN ? fminf(fminf(a, b), c) : fmaxf(fmaxf(a, b), c);
+            v[i] = MIN ? __builtin_elementwise_minimum(__builtin_elementwise_minimum(a, b), c)
+                       : __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
         }
         n = m;
     }
@@ -163,7 +166,7 @@ template <int NKB, int NDB>
 __device__ __attribute__((always_inline)) inline void tile_exp(f32x16 (&s)[NKB], f32x16 (&oacc)[NDB],
                                                                float& m_run, float& l_run, float mt,
                                                                float cc) {
-    const float m_cand = fmaxf(m_run, mt);
+    const float m_cand = __builtin_elementwise_maximum(m_run, mt);
     if (__any(m_cand > m_run + kRescaleThreshold)) {
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_cand);
         l_run *= alpha;
