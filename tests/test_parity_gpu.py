@@ -134,6 +134,26 @@ def test_large_magnitude_scores(dt):
         full_check(q, k, v, 0.125, causal, dt, f"{dt} large scores causal={causal}")
 
 
+@pytest.mark.parametrize("B,H,Nq,waves_br", [(1, 1, 4, (4, 64)), (4, 64, 128, (4, 128))])
+def test_fp16_denormal_weights(B, H, Nq, waves_br):
+    """Weights in the fp16 denormal range: one key has weight 1 and the 3000 others weight
+    2^-16 in every row, so together they raise l by 4.6% and L by 0.045. The PV product
+    takes them as fp16 denormals and l sums them in fp32; a path that flushed them would
+    miss that (the bound on L is 1e-3). Both forms of the 4-wave kernel (key split and
+    plain) are covered."""
+    Nk, d = 3001, 8
+    cfg = fa.fa_select_config("f16", B, H, Nq, Nk, d, False)
+    assert (cfg["waves"], cfg["Br"]) == waves_br, cfg
+    q = torch.zeros(B, H, Nq, d)
+    q[..., 0] = 1.0
+    k = torch.zeros(B, H, Nk, d)
+    k[:, :, 1:, 0] = -16.0 * math.log(2.0)          # score -16 ln 2: weight 2^-16 (scale 1)
+    v = make_random((B, H, Nk, d), "f32", 29)
+    q, k, v = q.half(), k.half(), v.half()
+    o, lse = full_check(q, k, v, 1.0, False, "f16", f"f16 denormal weights B={B} H={H} Nq={Nq}")
+    assert float(lse.double().min()) > 0.04        # the 3000 small weights are in l
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_increasing_scores_force_rescales(dt):
     """Scores that grow along the keys: every tile raises the row max by more than the
