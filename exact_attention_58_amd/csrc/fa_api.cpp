@@ -305,34 +305,58 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
         return FA_ELAUNCH;
     }
     fa_status result = FA_EUNSUPPORTED;
-    fa::TileConfig best{};
-    float best_ms = 0.0f;
-    for (const fa::TileConfig& c : cand) {
-        // one untimed launch; it also rejects configurations with no kernel for these inputs
+    // one untimed launch each; it also rejects configurations with no kernel for these inputs
+    bool admitted[4] = {false, false, false, false};
+    for (int i = 0; i < 4 && result != FA_ELAUNCH; ++i) {
         st = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
-                         stream, &c);
-        if (st == FA_EUNSUPPORTED) continue;
-        if (st != FA_OK) {
-            result = st;
-            break;
+                         stream, &cand[i]);
+        if (st == FA_OK) {
+            admitted[i] = true;
+            result = FA_OK;
+        } else if (st != FA_EUNSUPPORTED) {
+            result = FA_ELAUNCH;
         }
+    }
+    // times `n` launches of configuration c (ms), or a negative value on a HIP failure
+    auto timed = [&](const fa::TileConfig& c, int n) -> float {
         bool ok = hipEventRecord(e0, s) == hipSuccess;
-        for (int r = 0; ok && r < reps; ++r)
+        for (int r = 0; ok && r < n; ++r)
             ok = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
                              stream, &c) == FA_OK;
         ok = ok && hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess;
         float ms = 0.0f;
         ok = ok && hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
-        if (!ok) {
-            result = FA_ELAUNCH;
-            break;
-        }
-        if (result != FA_OK || ms < best_ms) {
-            best = c;
-            best_ms = ms;
-            result = FA_OK;
-        }
+        return ok ? ms : -1.0f;
+    };
+    // An idle GPU needs some milliseconds of work before its clock is up, and the first
+    // configuration timed would pay for it: launches of the first admitted configuration
+    // until about 20 ms of GPU time have passed. Then two rounds over every admitted
+    // configuration; each keeps its faster round.
+    int first = 0;
+    while (first < 4 && !admitted[first]) ++first;
+    float warm_ms = 0.0f;
+    for (int n = 0; result == FA_OK && warm_ms < 20.0f && n < 4096; n += 8) {
+        const float ms = timed(cand[first], 8);
+        if (ms < 0.0f) result = FA_ELAUNCH;
+        warm_ms += ms;
     }
+    float best_round[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int round = 0; round < 2 && result == FA_OK; ++round)
+        for (int i = 0; i < 4 && result == FA_OK; ++i) {
+            if (!admitted[i]) continue;
+            const float ms = timed(cand[i], reps);
+            if (ms < 0.0f) result = FA_ELAUNCH;
+            else if (round == 0 || ms < best_round[i]) best_round[i] = ms;
+        }
+    fa::TileConfig best{};
+    float best_ms = 0.0f;
+    bool have = false;
+    for (int i = 0; i < 4 && result == FA_OK; ++i)
+        if (admitted[i] && (!have || best_round[i] < best_ms)) {
+            best = cand[i];
+            best_ms = best_round[i];
+            have = true;
+        }
     if (result == FA_OK) {
         // o and lse end up holding the chosen configuration's result
         result = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal,

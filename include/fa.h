@@ -154,9 +154,11 @@ fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, fl
  * The pages' kernels pick tile sizes by hand and by search (page "Flash Attention Shared
  * Memory constraint", the group-size search; page "Add Fused Multi-Head Attention example":
  * its Python counterpart searches a space of hand-picked configurations). Here each
- * configuration fa_fwd_config accepts
- * runs once untimed and then `reps` times (1..1000) between two HIP events on `stream`;
- * the fastest is written to *Br, *Bc, *waves (each may be NULL) and remembered for this
+ * configuration fa_fwd_config accepts runs once untimed. The first of them then runs
+ * untimed for about 20 ms of GPU time, so that the GPU's clock has left its idle state.
+ * After that, two rounds time `reps` launches (1..1000) of every configuration between two
+ * HIP events on `stream`. Each configuration keeps its faster round, and the fastest
+ * configuration is written to *Br, *Bc, *waves (each may be NULL) and remembered for this
  * exact problem (current device, dtype, B, H, Nq, Nk, d, causal). Later fa_fwd calls on the
  * same problem launch it instead of the built-in choice, as long as the buffers allow it
  * (a ping-pong choice needs 16-byte aligned buffers). The record holds up to 256 problems;
