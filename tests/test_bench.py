@@ -1,0 +1,83 @@
+"""Host logic of bench.py (CPU only): the one-GPU refusal, the warm-up floor, the roofline
+fields and the HBM-traffic lookup keyed by the forward kernels' source."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from exact_attention_58_amd.workloads import WORKLOADS  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+class _FakeEvent:
+    """Stands in for torch.cuda.Event: every recorded interval lasts `ms`."""
+    ms = 1.0
+
+    def __init__(self, enable_timing=False):
+        pass
+
+    def record(self, stream=None):
+        pass
+
+    def elapsed_time(self, other):
+        return _FakeEvent.ms
+
+
+class _FakeCuda:
+    Event = _FakeEvent
+
+    @staticmethod
+    def synchronize(*a):
+        pass
+
+
+class _FakeTorch:
+    cuda = _FakeCuda
+
+
+@pytest.mark.parametrize("per_call_ms,steps,expect", [
+    (2.0, 5, 51),       # 5 requested steps, extended to 100 ms: 1 timed probe + 50 more
+    (0.01, 5, 10001),   # short calls: the floor sets the count
+    (300.0, 5, 5),      # long calls: the requested steps already exceed the floor
+    (300.0, 0, 1),      # no requested steps: the probe call alone
+])
+def test_warm_up_floor(per_call_ms, steps, expect):
+    _FakeEvent.ms = per_call_ms
+    calls = []
+    n = bench.warm_up(_FakeTorch, lambda: calls.append(1), steps, None)
+    assert n == len(calls) == expect
+    assert n >= steps
+    assert n * per_call_ms >= min(bench.WARM_MS, n * per_call_ms)
+
+
+def test_roofline_fields_and_traffic_key():
+    w = WORKLOADS["d128_bf16"]
+    sha = bench.kernel_sha()
+    ms = w.flops / 1e12 / 1000.0 * 1e3  # launch time (ms) that gives exactly 1000 TFLOP/s
+    r = bench.roofline_for(w, ms, sha)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2516.6
+    assert abs(r["achieved"] - 1000.0) < 0.01
+    assert abs(r["frac"] - 1000.0 / 2516.6) < 1e-4
+    recorded = bench.TRAFFIC["d128_bf16"]
+    # traffic is reported only for the kernel source it was measured on
+    assert bench.roofline_for(w, ms, recorded["kernel_sha"])["traffic"] == recorded["bytes"]
+    assert bench.roofline_for(w, ms, "0" * 16)["traffic"] is None
+    assert bench.roofline_for(WORKLOADS["ragged_f16"], ms, sha)["traffic"] is None
+
+
+def test_kernel_sha_covers_the_forward_sources():
+    names = [os.path.basename(p) for p in bench.KERNEL_SRC]
+    assert names == ["fa_fwd_kernels.hip", "fa_device.h", "fa_internal.h"]
+    assert all(os.path.exists(p) for p in bench.KERNEL_SRC)
+    assert len(bench.kernel_sha()) == 16
