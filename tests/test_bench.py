@@ -58,7 +58,7 @@ def test_warm_up_floor(per_call_ms, steps, expect):
     n = bench.warm_up(_FakeTorch, lambda: calls.append(1), steps, None)
     assert n == len(calls) == expect
     assert n >= steps
-    assert n * per_call_ms >= min(bench.WARM_MS, n * per_call_ms)
+    assert n * per_call_ms >= bench.WARM_MS  # the warm-up covers the floor
 
 
 def test_roofline_fields_and_traffic_key():
