@@ -748,11 +748,15 @@ __device__ inline f32x4 load_chunk32(const float* base, int row, int col, int nr
 
 // fp32 forward kernel on v_mfma_f32_32x32x2_f32. The head-dim reduction of S^T is
 // enumerated as d = h32*(DP/2) + ds so each lane loads half a contiguous row of Q
-// and of K. P stays fp32 for the PV product.
-template <int DP, int BC, bool CAUSAL, bool VEC>
+// and of K. P stays fp32 for the PV product. SPLIT = 2 (non-causal grids too small to
+// fill the chip) works as in the 16-bit kernel: 64 rows per workgroup, the two waves of a
+// row block each walk one half of the key tiles (one LDS tile buffer per half) and the
+// halves' (O, m, l) merge through LDS at the end.
+template <int DP, int BC, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd32_kernel(FwdArgs a, int n_qtiles) {
-    constexpr int NW = 4, BR = 32 * NW;
+    static_assert(SPLIT == 1 || (SPLIT == 2 && !CAUSAL), "key split: non-causal only");
+    constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB;
     constexpr int KST = DP + 4;  // floats; 16-byte pad
     constexpr int VST = DP;      // floats
     constexpr int CPR = DP / 4;
@@ -764,12 +768,15 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
 
     // Two K/V buffers when two workgroups still fit the CU's 160 KiB of LDS: tile j+1 is
     // stored while tile j is read, one barrier per tile. Otherwise one buffer, two barriers.
-    constexpr int NBUF = 2 * 2 * BC * (KST + VST) * 4 <= 160 * 1024 ? 2 : 1;
+    // The key split keeps one buffer per half.
+    constexpr int NBUF = SPLIT == 2 || 2 * 2 * BC * (KST + VST) * 4 <= 160 * 1024 ? 2 : 1;
     __shared__ __attribute__((aligned(16))) float Ks[NBUF][BC * KST];
     __shared__ __attribute__((aligned(16))) float Vs[NBUF][BC * VST];
+    static_assert(SPLIT == 1 || RB * (NDB * 16 + 2) * 64 <= NBUF * BC * KST, "merge fits the K buffers");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
+    const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
     const TileId wt = tile_of(a, n_qtiles, 64);
     const int bh = wt.bh;
@@ -780,7 +787,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     const int q0 = qt * BR;
     if (q0 >= Nq) return;  // a packed sequence shorter than the longest
     if (Nk == 0) return write_empty_rows<float>(a, sl, q0, BR);
-    const int r0w = q0 + wave * 32;
+    const int r0w = q0 + rbk * 32;
     const int myq = r0w + l32;
 
     const float* qg = (const float*)a.q + sl.q0 * d;
@@ -802,25 +809,28 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    f32x4 kreg[CH], vreg[CH];
-    auto load_tile = [&](int j) __attribute__((always_inline)) {
+    // staging of SPLIT tiles (one per key half; rows past Nk load as zeros)
+    f32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
+    auto load_tile_h = [&](int h, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
             const int chunk = tid + cc * 64 * NW;
             const int row = chunk / CPR, col = (chunk % CPR) * 4;
-            kreg[cc] = load_chunk32<VEC>(kg, j * BC + row, col, Nk, d);
-            vreg[cc] = load_chunk32<VEC>(vg, j * BC + row, col, Nk, d);
+            kreg[h][cc] = load_chunk32<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+            vreg[h][cc] = load_chunk32<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
         }
     };
-    auto store_tile = [&](int b) __attribute__((always_inline)) {
+    auto store_tile_h = [&](int h, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
             const int chunk = tid + cc * 64 * NW;
             const int row = chunk / CPR, col = (chunk % CPR) * 4;
-            *(f32x4*)(Ks[b] + row * KST + col) = kreg[cc];
-            *(f32x4*)(Vs[b] + row * VST + col) = vreg[cc];
+            *(f32x4*)(Ks[b] + row * KST + col) = kreg[h][cc];
+            *(f32x4*)(Vs[b] + row * VST + col) = vreg[h][cc];
         }
     };
+    auto load_tile = [&](int j) __attribute__((always_inline)) { load_tile_h(0, j); };
+    auto store_tile = [&](int b) __attribute__((always_inline)) { store_tile_h(0, b); };
 
     f32x16 oacc[NDB];
 #pragma unroll
@@ -871,7 +881,48 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
                 }
         }
     };
-    if constexpr (NBUF == 2) {
+    if constexpr (SPLIT == 2) {
+        // step i stages tile h * n_steps + i of each half h into buffer h
+        const int n_steps = (n_tiles + 1) / 2;
+        load_tile_h(0, 0);
+        load_tile_h(1, n_steps);
+        for (int i = 0; i < n_steps; ++i) {
+            __syncthreads();
+            store_tile_h(0, 0);
+            store_tile_h(1, 1);
+            __syncthreads();
+            if (i + 1 < n_steps) {
+                load_tile_h(0, i + 1);
+                load_tile_h(1, n_steps + i + 1);
+            }
+            const int j = half * n_steps + i;
+            if (j < n_tiles) tile(j, Ks[half], Vs[half]);  // the second half may have one tile less
+        }
+        // merge the key halves: half 1 hands (O, m, l) to half 0 through LDS (lane-contiguous
+        // rows of 64 floats)
+        constexpr int NV = NDB * 16 + 2;
+        float* mrg = &Ks[0][0] + rbk * NV * 64;
+        __syncthreads();  // every wave is done with the tile buffers
+        if (half == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mrg[(db * 16 + r) * 64 + lane] = oacc[db][r];
+            mrg[(NV - 2) * 64 + lane] = m_run;
+            mrg[(NV - 1) * 64 + lane] = l_run;
+        }
+        __syncthreads();
+        if (half == 1) return;
+        const float m2 = mrg[(NV - 2) * 64 + lane], l2 = mrg[(NV - 1) * 64 + lane];
+        const float m = fmaxf(m_run, m2);  // finite: half 0 has seen key tile 0
+        const float a1 = __builtin_amdgcn_exp2f(m_run - m), a2 = __builtin_amdgcn_exp2f(m2 - m);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a1 + mrg[(db * 16 + r) * 64 + lane] * a2;
+        l_run = l_run * a1 + l2 * a2;
+        m_run = m;
+    } else if constexpr (NBUF == 2) {
         load_tile(0);
         store_tile(0);
         __syncthreads();
@@ -951,13 +1002,19 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
 }
 
 template <int DP, int BC>
-static int launch32(const FwdArgs& a, bool vec, hipStream_t st) {
+static int launch32(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
     if (a.causal) {
-        return vec ? launch(fwd32_kernel<DP, BC, true, true>, a, 128, st, 256)
-                   : launch(fwd32_kernel<DP, BC, true, false>, a, 128, st, 256);
+        return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256)
+                   : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256);
     }
-    return vec ? launch(fwd32_kernel<DP, BC, false, true>, a, 128, st, 256)
-               : launch(fwd32_kernel<DP, BC, false, false>, a, 128, st, 256);
+    if constexpr (DP <= 96) {
+        if (cfg.br == 64) {  // key split (non-causal, d <= 96: checked by the caller)
+            return vec ? launch(fwd32_kernel<DP, BC, false, true, 2>, a, 64, st, 256)
+                       : launch(fwd32_kernel<DP, BC, false, false, 2>, a, 64, st, 256);
+        }
+    }
+    return vec ? launch(fwd32_kernel<DP, BC, false, true, 1>, a, 128, st, 256)
+               : launch(fwd32_kernel<DP, BC, false, false, 1>, a, 128, st, 256);
 }
 
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) {
@@ -977,10 +1034,10 @@ int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) 
         }
     }
     switch (cfg.dpad) {
-        case 32: return launch32<32, 64>(a, vec, st);
-        case 64: return launch32<64, 64>(a, vec, st);
-        case 96: return launch32<96, 64>(a, vec, st);
-        case 128: return launch32<128, 32>(a, vec, st);
+        case 32: return launch32<32, 64>(a, cfg, vec, st);
+        case 64: return launch32<64, 64>(a, cfg, vec, st);
+        case 96: return launch32<96, 64>(a, cfg, vec, st);
+        case 128: return launch32<128, 32>(a, cfg, vec, st);
         default: return (int)hipErrorInvalidValue;
     }
 }
