@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67528709, "kernel_sha": "4a742a37052d88c8"},
+    "pages_f32": {"bytes": 67520549, "kernel_sha": "d8decdfc65bdab17"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269675746, "kernel_sha": "4a742a37052d88c8"},
+    "d128_bf16": {"bytes": 269682920, "kernel_sha": "d8decdfc65bdab17"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 304844645, "kernel_sha": "4a742a37052d88c8"},
+    "d128_bf16_causal": {"bytes": 304615547, "kernel_sha": "d8decdfc65bdab17"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78283974, "kernel_sha": "4a742a37052d88c8"},
+    "long_causal_bf16": {"bytes": 78281121, "kernel_sha": "d8decdfc65bdab17"},
 }
 
 
