@@ -60,7 +60,7 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (cfg.dpad != dpad) return false;
     if (dtype == FA_F32)
         return cfg.waves == 4 && cfg.bc == (dpad > 96 ? 32 : 64) &&
-               (cfg.br == 128 || (cfg.br == 64 && !causal && dpad <= 96));
+               (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
     if (cfg.bc != 64) return false;
     if (cfg.waves == 8) return cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
     if (cfg.waves != 4) return false;
@@ -128,9 +128,9 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
     c.br = 32 * c.waves;
     if (dtype == FA_F32) {
         c.bc = c.dpad > 96 ? 32 : 64;
-        // too few 128-row workgroups to fill the chip: the key split, as for 16-bit inputs
+        // too few 128-row workgroups to fill the chip: the key split, also for causal grids
         // (d <= 96: at d = 128 the split's two staged tiles no longer fit the registers)
-        if (!causal && c.dpad <= 96 && (Nq + 127) / 128 * B * H < num_cus && Nk > 2 * c.bc) c.br = 64;
+        if (c.dpad <= 96 && (Nq + 127) / 128 * B * H < num_cus && Nk > 2 * c.bc) c.br = 64;
     } else {
         c.bc = 64;
         // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte

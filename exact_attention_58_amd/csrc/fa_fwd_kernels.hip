@@ -748,14 +748,17 @@ __device__ inline f32x4 load_chunk32(const float* base, int row, int col, int nr
 
 // fp32 forward kernel on v_mfma_f32_32x32x2_f32. The head-dim reduction of S^T is
 // enumerated as d = h32*(DP/2) + ds so each lane loads half a contiguous row of Q
-// and of K. P stays fp32 for the PV product. SPLIT = 2 (non-causal grids too small to
-// fill the chip) works as in the 16-bit kernel: 64 rows per workgroup, the two waves of a
-// row block each walk one half of the key tiles (one LDS tile buffer per half) and the
-// halves' (O, m, l) merge through LDS at the end.
+// and of K. P stays fp32 for the PV product. SPLIT = 2 (grids too small to fill the chip)
+// works as in the 16-bit kernel: 64 rows per workgroup, the two waves of a row block each
+// walk one half of the key tiles (one LDS tile buffer per half) and the halves' (O, m, l)
+// merge through LDS at the end. Causal grids may split too: a workgroup's rows start at
+// q0 = 64 t and its tiles end at its diagonal, so the second half starts at key
+// 64 ceil((t + 1) / 2) <= q0 and every row sees a key of the first tile it processes (for
+// t = 0 the second half has no tile and merges as zero weight).
 template <int DP, int BC, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd32_kernel(FwdArgs a, int n_qtiles) {
-    static_assert(SPLIT == 1 || (SPLIT == 2 && !CAUSAL), "key split: non-causal only");
+    static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
     constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB;
     constexpr int KST = DP + 4;  // floats; 16-byte pad
     constexpr int VST = DP;      // floats
@@ -1003,15 +1006,18 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
 
 template <int DP, int BC>
 static int launch32(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
-    if (a.causal) {
-        return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256)
-                   : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256);
-    }
     if constexpr (DP <= 96) {
-        if (cfg.br == 64) {  // key split (non-causal, d <= 96: checked by the caller)
+        if (cfg.br == 64) {  // key split (d <= 96: checked by the caller)
+            if (a.causal)
+                return vec ? launch(fwd32_kernel<DP, BC, true, true, 2>, a, 64, st, 256)
+                           : launch(fwd32_kernel<DP, BC, true, false, 2>, a, 64, st, 256);
             return vec ? launch(fwd32_kernel<DP, BC, false, true, 2>, a, 64, st, 256)
                        : launch(fwd32_kernel<DP, BC, false, false, 2>, a, 64, st, 256);
         }
+    }
+    if (a.causal) {
+        return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256)
+                   : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256);
     }
     return vec ? launch(fwd32_kernel<DP, BC, false, true, 1>, a, 128, st, 256)
                : launch(fwd32_kernel<DP, BC, false, false, 1>, a, 128, st, 256);

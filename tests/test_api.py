@@ -103,7 +103,6 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
     ((128, 64, 4), dict(dtype=0, d=128)),      # fp32 d > 96 uses 32-key tiles
     ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys
     ((64, 64, 4), dict(causal=1)),             # the key split is non-causal only
-    ((64, 64, 4), dict(dtype=0, causal=1)),    # for fp32 too
     ((64, 32, 4), dict(dtype=0, d=128)),       # no fp32 key split above d = 96
     ((64, 64, 4), dict(d=128)),                # and d <= 96 only
     ((256, 64, 8), dict(d=136)),               # ping-pong only up to d = 128
@@ -240,12 +239,13 @@ def test_select_config_grid_fill(dtype):
 
 
 def test_select_config_fp32_key_split():
-    """fp32 grids too small to fill the chip take the two-way key split (non-causal)."""
+    """fp32 grids too small to fill the chip take the two-way key split (causal too)."""
     small = fa.fa_select_config("f32", 1, 8, 1024, 1024, 64, False, num_cus=256)
     assert (small["Br"], small["Bc"], small["waves"]) == (64, 64, 4)
     small128 = fa.fa_select_config("f32", 1, 8, 1024, 1024, 128, False, num_cus=256)
     assert (small128["Br"], small128["Bc"]) == (128, 32)  # no split above d = 96
-    assert fa.fa_select_config("f32", 1, 8, 1024, 1024, 64, True, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config("f32", 1, 8, 1024, 1024, 64, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 1, 1, 256, 256, 64, True, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 4, 4, 4096, 4096, 64, False, num_cus=256)["Br"] == 128
     assert fa.fa_select_config("f32", 1, 8, 1024, 128, 64, False, num_cus=256)["Br"] == 128
 

@@ -45,7 +45,7 @@ def admitted(dt, d, causal):
     dpad = (d + 31) // 32 * 32
     if dt == "f32":
         bc = 32 if dpad > 96 else 64
-        split = [] if causal or dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}]
+        split = [] if dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}]
         return [{"Br": 128, "Bc": bc, "waves": 4}] + split
     out = [{"Br": 128, "Bc": 64, "waves": 4}]
     if d % 8 == 0 and dpad <= 128:
