@@ -222,7 +222,7 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 
 // 16-bit forward kernel. DP: padded head dim (32, 64, 96, 128). Workgroup = 4 waves; K/V
 // tiles of 64 keys. SPLIT = 1: 4 row blocks of 32 = 128 query rows, every wave walks all
-// key tiles. SPLIT = 2 (non-causal grids too small to fill the chip): 2 row blocks = 64
+// key tiles. SPLIT = 2 (grids too small to fill the chip): 2 row blocks = 64
 // rows, and the two waves of a row block each walk one half of the key tiles (two tiles
 // staged per step); at the end the second half's (O, m, l) pass through LDS and the first
 // half merges them: m = max(m1, m2), l = l1 2^(m1-m) + l2 2^(m2-m), O likewise, the same
@@ -231,7 +231,11 @@ template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DP > 128 ? 1 : 2, DP > 128 ? 1 : 2)))
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
-    static_assert(SPLIT == 1 || (SPLIT == 2 && !CAUSAL), "key split: non-causal only");
+    // Causal grids split too: a workgroup's rows start at q0 = 64 t and its key tiles end at
+    // its diagonal, so the second half starts at key 64 ceil((t + 1) / 2) <= q0 and every row
+    // sees a key of the first tile it processes (for t = 0 the second half has no tile and
+    // merges as zero weight).
+    static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
     constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB, BC = 64;
     constexpr int KST = DP + 8;   // K row stride (elements): 16-byte pad, conflict-free b128 reads
     // V row stride: 4 consecutive rows must start in 4 distinct quarters of the 16 bank groups
@@ -990,15 +994,18 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
             return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
         }
     }
-    if (a.causal) {
-        return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256)
-                   : launch(fwd16_kernel<T, DP, true, false, 1>, a, 128, st, 256);
-    }
     if constexpr (DP <= 96) {
-        if (cfg.br == 64) {  // key split in two (non-causal, small grids)
+        if (cfg.br == 64) {  // key split in two (small grids)
+            if (a.causal)
+                return vec ? launch(fwd16_kernel<T, DP, true, true, 2>, a, 64, st, 256)
+                           : launch(fwd16_kernel<T, DP, true, false, 2>, a, 64, st, 256);
             return vec ? launch(fwd16_kernel<T, DP, false, true, 2>, a, 64, st, 256)
                        : launch(fwd16_kernel<T, DP, false, false, 2>, a, 64, st, 256);
         }
+    }
+    if (a.causal) {
+        return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256)
+                   : launch(fwd16_kernel<T, DP, true, false, 1>, a, 128, st, 256);
     }
     return vec ? launch(fwd16_kernel<T, DP, false, true, 1>, a, 128, st, 256)
                : launch(fwd16_kernel<T, DP, false, false, 1>, a, 128, st, 256);
