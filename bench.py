@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67512372, "kernel_sha": "e86458dc345a5fea"},
+    "pages_f32": {"bytes": 67529792, "kernel_sha": "07b63a70a7633585"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269682962, "kernel_sha": "e86458dc345a5fea"},
+    "d128_bf16": {"bytes": 269681920, "kernel_sha": "07b63a70a7633585"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 305385098, "kernel_sha": "e86458dc345a5fea"},
+    "d128_bf16_causal": {"bytes": 305760149, "kernel_sha": "07b63a70a7633585"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78282751, "kernel_sha": "e86458dc345a5fea"},
+    "long_causal_bf16": {"bytes": 78281287, "kernel_sha": "07b63a70a7633585"},
 }
 
 
