@@ -53,7 +53,7 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
 
 // Whether `cfg` names a kernel that exists for these inputs: the 16-bit kernels are the
 // ping-pong kernel (8 waves, 256 rows: 16-byte rows, d % 8 == 0, d <= 128), the 4-wave kernel
-// (128 rows) and its key-split form (64 rows: d <= 96); fp32 has one kernel per head dim
+// (128 rows) and its key-split form (64 rows: d <= 128); fp32 has one kernel per head dim
 // and its key-split form (64 rows: d <= 96). The tile keys and the padded head dim are fixed
 // by dtype and d.
 bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool aligned) {
@@ -66,7 +66,7 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (cfg.waves == 8) return cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
     if (cfg.waves != 4) return false;
     if (cfg.br == 128) return true;
-    return cfg.br == 64 && dpad <= 96;
+    return cfg.br == 64 && dpad <= 128;
 }
 
 // Configurations fa_tune_fwd measured fastest, one per exact problem (device, dtype, sizes,
@@ -154,7 +154,7 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         } else if (aligned && d % 8 == 0 && d > 32 && wgs256 >= num_cus && Nk > pp_min_keys) {
             c.waves = 8;
             c.br = 256;
-        } else if (c.dpad <= 96 && wgs128 < num_cus && Nk > 2 * c.bc) {
+        } else if (c.dpad <= 128 && wgs128 < num_cus && Nk > 2 * c.bc) {
             // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
             // block's keys walked in two halves by two waves and merged at the end
             c.br = 64;

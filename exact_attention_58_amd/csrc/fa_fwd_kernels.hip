@@ -220,7 +220,7 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
     return sum;
 }
 
-// 16-bit forward kernel. DP: padded head dim (32, 64, 96, 128). Workgroup = 4 waves; K/V
+// 16-bit forward kernel. DP: padded head dim (32 ... 256). Workgroup = 4 waves; K/V
 // tiles of 64 keys. SPLIT = 1: 4 row blocks of 32 = 128 query rows, every wave walks all
 // key tiles. SPLIT = 2 (grids too small to fill the chip): 2 row blocks = 64
 // rows, and the two waves of a row block each walk one half of the key tiles (two tiles
@@ -994,7 +994,7 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
             return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
         }
     }
-    if constexpr (DP <= 96) {
+    if constexpr (DP <= 128) {
         if (cfg.br == 64) {  // key split in two (small grids)
             if (a.causal)
                 return vec ? launch(fwd16_kernel<T, DP, true, true, 2>, a, 64, st, 256)

@@ -137,7 +137,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  * Br, Bc, waves: query rows per workgroup, keys per K/V tile and waves per workgroup, as
  * fa_select_config and fa_tune_fwd report them. The kernels that exist: for fp16/bf16,
  * (256, 64, 8) when every buffer is 16-byte aligned, d % 8 == 0 and d <= 128; (128, 64, 4);
- * (64, 64, 4), the two-way key split, when d <= 96. For fp32, (128, 64, 4) for d <= 96 and
+ * (64, 64, 4), the two-way key split, when d <= 128. For fp32, (128, 64, 4) for d <= 96 and
  * (128, 32, 4) above, and (64, 64, 4) when d <= 96. Any other triple returns
  * FA_EUNSUPPORTED before any HIP call.
  * Everything else (arguments, ownership, errors) is as for fa_fwd; the result is the same

@@ -103,7 +103,7 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
     ((128, 64, 4), dict(dtype=0, d=128)),      # fp32 d > 96 uses 32-key tiles
     ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys
     ((64, 32, 4), dict(dtype=0, d=128)),       # no fp32 key split above d = 96
-    ((64, 64, 4), dict(d=128)),                # and d <= 96 only
+    ((64, 64, 4), dict(d=136)),                # the 16-bit key split stops at d = 128
     ((256, 64, 8), dict(d=136)),               # ping-pong only up to d = 128
     ((256, 64, 8), dict(d=60)),                # and for d % 8 == 0
     ((256, 64, 8), dict(q=P + 2)),             # and for 16-byte aligned rows
@@ -213,7 +213,7 @@ def test_select_config_grid_fill(dtype):
     small_causal = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, True, num_cus=256)
     assert small_causal["waves"] == 4 and small_causal["Br"] == 64  # causal grids split too
     small_d128 = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 128, False, num_cus=256)
-    assert small_d128["Br"] == 128
+    assert small_d128["Br"] == 64  # the key split reaches d = 128 for 16-bit inputs
     # enough 128-row workgroups (d % 8 != 0 keeps the 256-row kernel out): no key split
     filled = fa.fa_select_config(dtype, 4, 16, 1000, 3001, 90, False, num_cus=256)
     assert filled["Br"] == 128

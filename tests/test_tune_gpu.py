@@ -50,7 +50,7 @@ def admitted(dt, d, causal):
     out = [{"Br": 128, "Bc": 64, "waves": 4}]
     if d % 8 == 0 and dpad <= 128:
         out.append({"Br": 256, "Bc": 64, "waves": 8})
-    if dpad <= 96:
+    if dpad <= 128:
         out.append({"Br": 64, "Bc": 64, "waves": 4})
     return out
 
