@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67529792, "kernel_sha": "07b63a70a7633585"},
+    "pages_f32": {"bytes": 67520555, "kernel_sha": "99de4aa0066d59d9"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269681920, "kernel_sha": "07b63a70a7633585"},
+    "d128_bf16": {"bytes": 269682904, "kernel_sha": "99de4aa0066d59d9"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 305760149, "kernel_sha": "07b63a70a7633585"},
+    "d128_bf16_causal": {"bytes": 305906512, "kernel_sha": "99de4aa0066d59d9"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78281287, "kernel_sha": "07b63a70a7633585"},
+    "long_causal_bf16": {"bytes": 78280707, "kernel_sha": "99de4aa0066d59d9"},
 }
 
 
