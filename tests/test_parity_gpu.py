@@ -93,7 +93,7 @@ def test_workload(name):
 SWEEP = []
 for dt in ("bf16", "f16", "f32"):
     for d in (32, 64, 96, 128, 40, 5):
-        for (Nq, Nk) in ((1, 1), (17, 63), (64, 65), (129, 127), (200, 1000), (300, 300)):
+        for (Nq, Nk) in ((1, 1), (17, 63), (64, 65), (129, 127), (200, 1000), (300, 300), (1000, 300)):
             for causal in (False, True):
                 SWEEP.append((dt, d, Nq, Nk, causal))
 # head dims past 128 (16-bit only)
