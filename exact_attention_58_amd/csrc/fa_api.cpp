@@ -129,9 +129,11 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
     c.br = 32 * c.waves;
     if (dtype == FA_F32) {
         c.bc = c.dpad > 96 ? 32 : 64;
-        // too few 128-row workgroups to fill the chip: the key split, also for causal grids
-        // (d <= 96: at d = 128 the split's two staged tiles no longer fit the registers)
-        if (c.dpad <= 96 && (Nq + 127) / 128 * B * H < num_cus && Nk > 2 * c.bc) c.br = 64;
+        // fewer 128-row workgroups than the chip holds (two per CU): the key split, also for
+        // causal grids (measured below 2 per CU: B1 H20 N2048 d64 265 -> 221 us, causal
+        // B1 H40 N1024 97 -> 74 us). d <= 96: at d = 128 the split's two staged tiles no
+        // longer fit the registers.
+        if (c.dpad <= 96 && (Nq + 127) / 128 * B * H < 2 * num_cus && Nk > 2 * c.bc) c.br = 64;
     } else {
         c.bc = 64;
         // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte
@@ -154,9 +156,14 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         } else if (aligned && d % 8 == 0 && d > 32 && wgs256 >= num_cus && Nk > pp_min_keys) {
             c.waves = 8;
             c.br = 256;
-        } else if (c.dpad <= 128 && wgs128 < num_cus && Nk > 2 * c.bc) {
+        } else if (c.dpad <= 128 && (wgs128 < num_cus || (causal && wgs128 < 2 * num_cus)) &&
+                   Nk > 2 * c.bc) {
             // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
-            // block's keys walked in two halves by two waves and merged at the end
+            // block's keys walked in two halves by two waves and merged at the end. Causal
+            // grids split up to two workgroups per CU: their uneven workgroups leave a tail
+            // that the split halves (B1 H20 N2048 d64 causal: 46.1 -> 33.2 us). Non-causal
+            // grids between one and two per CU measured slower split (B1 H56 N1024 d128:
+            // 45.4 vs 59.9 us).
             c.br = 64;
         }
     }

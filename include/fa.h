@@ -224,7 +224,8 @@ const char* fa_status_str(fa_status s);
  * the padded head dimension the kernel is compiled for (*dpad). Any output
  * pointer may be NULL. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
  * `num_cus` is the device's compute-unit count (256 on MI355X); it only
- * affects the query-tile height when the grid would not fill the chip. Key
+ * affects the query-tile height: grids of fewer 128-row workgroups than CUs
+ * (than two per CU for causal grids and for fp32) take the two-way key split. Key
  * sequences of at most 512 keys (HBM-bound) use the 4-wave, 128-row kernel. The
  * answer assumes 16-byte aligned buffers; fa_fwd on unaligned buffers (or a
  * 16-bit d that is not a multiple of 8) uses the 4-wave, 128-row kernel.

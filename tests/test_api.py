@@ -212,6 +212,10 @@ def test_select_config_grid_fill(dtype):
     assert small["waves"] == 4 and small["Br"] == 64
     small_causal = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, True, num_cus=256)
     assert small_causal["waves"] == 4 and small_causal["Br"] == 64  # causal grids split too
+    # between one and two 128-row workgroups per CU: causal grids split, non-causal do not
+    assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config(dtype, 1, 40, 2048, 2048, 64, True, num_cus=256)["Br"] == 128
     small_d128 = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 128, False, num_cus=256)
     assert small_d128["Br"] == 64  # the key split reaches d = 128 for 16-bit inputs
     # enough 128-row workgroups (d % 8 != 0 keeps the 256-row kernel out): no key split
@@ -246,6 +250,9 @@ def test_select_config_fp32_key_split():
     assert fa.fa_select_config("f32", 1, 8, 1024, 1024, 64, True, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 1, 1, 256, 256, 64, True, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 4, 4, 4096, 4096, 64, False, num_cus=256)["Br"] == 128
+    # up to two 128-row workgroups per CU (fp32, causal or not)
+    assert fa.fa_select_config("f32", 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 1, 40, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
     assert fa.fa_select_config("f32", 1, 8, 1024, 128, 64, False, num_cus=256)["Br"] == 128
 
 

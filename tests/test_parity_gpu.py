@@ -154,6 +154,17 @@ def test_fp16_denormal_weights(B, H, Nq, waves_br):
     assert float(lse.double().min()) > 0.04        # the 3000 small weights are in l
 
 
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("f16", True), ("f32", False), ("f32", True)])
+def test_key_split_up_to_two_workgroups_per_cu(dt, causal):
+    """Grids of 320 128-row workgroups (between one and two per CU) take the two-way key
+    split for causal 16-bit and for fp32 inputs: every row against the oracle."""
+    B, H, N, d = 1, 20, 2048, 64
+    cfg = fa.fa_select_config(dt, B, H, N, N, d, causal)
+    assert (cfg["waves"], cfg["Br"]) == (4, 64), cfg
+    q, k, v = (make_random((B, H, N, d), dt, 900 + i) for i in range(3))
+    full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} split B1 H20 N2048 causal={causal}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_increasing_scores_force_rescales(dt):
     """Scores that grow along the keys: every tile raises the row max by more than the
