@@ -72,11 +72,11 @@ def lib():
             L.fa_fwd_config.restype = ctypes.c_int
             L.fa_fwd_config.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                        ctypes.c_int, vp]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
             ip_ = ctypes.POINTER(ctypes.c_int)
             L.fa_tune_fwd.restype = ctypes.c_int
             L.fa_tune_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
-                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ip_, ip_, ip_]
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ip_, ip_, ip_, ip_, ip_]
             L.fa_tune_clear.restype = None
             L.fa_tune_clear.argtypes = []
             L.fa_bwd.restype = ctypes.c_int
@@ -181,14 +181,17 @@ def _stream_handle(stream, dev):
 
 
 def fa_fwd_config(q, k, v, o, lse, scale: float, causal: bool, cfg: dict, stream=None) -> None:
-    """fa_fwd with an explicit tile configuration (a dict with Br, Bc, waves)."""
+    """fa_fwd with an explicit tile configuration: a dict with Br, Bc, waves and optionally
+    the knobs occ (workgroups per CU, 0 = no cap) and group (causal dispatch group, 0 =
+    built-in), as fa_tune_fwd returns it."""
     import torch
     B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
     handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         rc = lib().fa_fwd_config(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                  B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
-                                 int(cfg["Br"]), int(cfg["Bc"]), int(cfg["waves"]), handle)
+                                 int(cfg["Br"]), int(cfg["Bc"]), int(cfg["waves"]),
+                                 int(cfg.get("occ", 0)), int(cfg.get("group", 0)), handle)
     if rc != FA_OK:
         raise FaError(rc, "fa_fwd_config")
 
@@ -199,14 +202,14 @@ def fa_tune_fwd(q, k, v, o, lse, scale: float, causal: bool, reps: int = 10, str
     import torch
     B, H, Nq, Nk, d = _check_dense(q, k, v, o, lse)
     handle = _stream_handle(stream, q.device)
-    out = [ctypes.c_int(0) for _ in range(3)]
+    out = [ctypes.c_int(0) for _ in range(5)]
     with torch.cuda.device(q.device):
         rc = lib().fa_tune_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
                                int(reps), handle, *[ctypes.byref(x) for x in out])
     if rc != FA_OK:
         raise FaError(rc, "fa_tune_fwd")
-    return dict(zip(("Br", "Bc", "waves"), (x.value for x in out)))
+    return dict(zip(("Br", "Bc", "waves", "occ", "group"), (x.value for x in out)))
 
 
 def fa_tune_clear() -> None:

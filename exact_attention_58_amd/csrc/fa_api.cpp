@@ -59,6 +59,8 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
 bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool aligned) {
     const int dpad = (int)((d + 31) / 32) * 32;
     if (cfg.dpad != dpad) return false;
+    if (cfg.occ < 0 || cfg.occ > 4) return false;
+    if (cfg.group != 0 && (cfg.group < 8 || cfg.group > 1024)) return false;
     if (dtype == FA_F32)
         return cfg.waves == 4 && cfg.bc == (dpad > 96 ? 32 : 64) &&
                (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
@@ -221,6 +223,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     a.cu_k = cu_k;
     a.tq = tq;
     a.tk = tk;
+    a.slots = cfg.group;
     return launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
@@ -290,26 +293,27 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
 
 fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                         int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
-                        fa_dtype dtype, int Br, int Bc, int waves, void* stream) {
+                        fa_dtype dtype, int Br, int Bc, int waves, int occ, int group, void* stream) {
     if (!q || !k || !v || !o || !lse) return FA_EINVAL;
     if (!std::isfinite(scale)) return FA_EINVAL;
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
-    fa::TileConfig cfg{Br, Bc, waves, (int)((d + 31) / 32) * 32};
+    fa::TileConfig cfg{Br, Bc, waves, (int)((d + 31) / 32) * 32, occ, group};
     return fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
                        stream, &cfg);
 }
 
 fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                       int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale, int causal,
-                      fa_dtype dtype, int reps, void* stream, int* Br, int* Bc, int* waves) {
+                      fa_dtype dtype, int reps, void* stream, int* Br, int* Bc, int* waves, int* occ,
+                      int* group) {
     if (!q || !k || !v || !o || !lse) return FA_EINVAL;
     if (!std::isfinite(scale) || reps < 1 || reps > 1000) return FA_EINVAL;
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
     const int dpad = (int)((d + 31) / 32) * 32;
-    const fa::TileConfig cand[4] = {{256, 64, 8, dpad}, {128, 64, 4, dpad}, {64, 64, 4, dpad},
-                                    {128, dpad > 96 ? 32 : 64, 4, dpad}};
+    const fa::TileConfig cand[4] = {{256, 64, 8, dpad, 0, 0}, {128, 64, 4, dpad, 0, 0},
+                                    {64, 64, 4, dpad, 0, 0}, {128, dpad > 96 ? 32 : 64, 4, dpad, 0, 0}};
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;
@@ -370,6 +374,36 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
             best_ms = best_round[i];
             have = true;
         }
+    // Then the knobs, one at a time from the chosen tiles (their results are bit-identical):
+    // one workgroup per CU for the 4-wave kernels (two fit otherwise), and for causal grids
+    // the dispatch group size. Two rounds again, the chosen tiles timed beside them.
+    constexpr int kKnobs = 6;
+    fa::TileConfig knob[kKnobs];
+    int n_knob = 0;
+    if (result == FA_OK) {
+        knob[n_knob++] = best;
+        if (best.waves == 4) {
+            knob[n_knob] = best;
+            knob[n_knob++].occ = 1;
+        }
+        if (causal)
+            for (int g : {16, 32, 64, 128}) {
+                knob[n_knob] = best;
+                knob[n_knob++].group = g;
+            }
+    }
+    float knob_ms[kKnobs] = {};
+    for (int round = 0; round < 2 && result == FA_OK && n_knob > 1; ++round)
+        for (int i = 0; i < n_knob && result == FA_OK; ++i) {
+            const float ms = timed(knob[i], reps);
+            if (ms < 0.0f) result = FA_ELAUNCH;
+            else if (round == 0 || ms < knob_ms[i]) knob_ms[i] = ms;
+        }
+    for (int i = 1; i < n_knob && result == FA_OK; ++i)
+        if (knob_ms[i] < knob_ms[0]) {
+            best = knob[i];
+            knob_ms[0] = knob_ms[i];
+        }
     if (result == FA_OK) {
         // o and lse end up holding the chosen configuration's result
         result = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal,
@@ -382,6 +416,8 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
         if (Br) *Br = best.br;
         if (Bc) *Bc = best.bc;
         if (waves) *waves = best.waves;
+        if (occ) *occ = best.occ;
+        if (group) *group = best.group;
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);

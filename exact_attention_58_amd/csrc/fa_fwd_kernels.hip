@@ -83,6 +83,7 @@ struct TileId {
 // slots: workgroups of the calling kernel an XCD holds at once (32 CUs x workgroups per CU).
 __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles, int slots) {
     const int i = blockIdx.x;
+    if (a.slots > 0) slots = a.slots;
     const PairTile pt = xcd_pair_tile(i, gridDim.x, n_qtiles, a.B * a.H, a.causal, slots);
     if (a.cu_q != nullptr && (a.B * a.H) % 8 == 0) {
         // XCD x takes pairs x, x + 8, x + 16, ...: its m-th pair is the m-th of its run above
@@ -978,11 +979,24 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
 
 // ---------------------------------------------------------------- launch
 
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+// occ > 0 caps the workgroups a CU holds at once: each launch also reserves unused dynamic
+// LDS so that one workgroup's share is kLdsPerCu / occ (no reservation when the kernel's
+// own LDS already exceeds that share).
 template <typename K>
-static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st, int threads) {
+static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st, int threads, int occ) {
     const int n_qtiles = (a.Nq + br - 1) / br;
     const int64_t total = (int64_t)n_qtiles * a.B * a.H;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(threads), 0, st, a, n_qtiles);
+    size_t dyn = 0;
+    if (occ > 0) {
+        hipFuncAttributes attr;
+        const hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel));
+        if (e != hipSuccess) return (int)e;
+        const size_t share = kLdsPerCu / (size_t)occ;
+        if (share > attr.sharedSizeBytes) dyn = share - attr.sharedSizeBytes;
+    }
+    hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(threads), dyn, st, a, n_qtiles);
     return (int)hipGetLastError();
 }
 
@@ -990,25 +1004,25 @@ template <typename T, int DP>
 static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
     if constexpr (DP <= 128) {
         if (cfg.waves == 8) {  // aligned, d % 8 == 0 (checked by the caller)
-            if (a.causal) return launch(fwd16_pp_kernel<T, DP, true>, a, cfg.br, st, 512);
-            return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512);
+            if (a.causal) return launch(fwd16_pp_kernel<T, DP, true>, a, cfg.br, st, 512, cfg.occ);
+            return launch(fwd16_pp_kernel<T, DP, false>, a, cfg.br, st, 512, cfg.occ);
         }
     }
     if constexpr (DP <= 128) {
         if (cfg.br == 64) {  // key split in two (small grids)
             if (a.causal)
-                return vec ? launch(fwd16_kernel<T, DP, true, true, 2>, a, 64, st, 256)
-                           : launch(fwd16_kernel<T, DP, true, false, 2>, a, 64, st, 256);
-            return vec ? launch(fwd16_kernel<T, DP, false, true, 2>, a, 64, st, 256)
-                       : launch(fwd16_kernel<T, DP, false, false, 2>, a, 64, st, 256);
+                return vec ? launch(fwd16_kernel<T, DP, true, true, 2>, a, 64, st, 256, cfg.occ)
+                           : launch(fwd16_kernel<T, DP, true, false, 2>, a, 64, st, 256, cfg.occ);
+            return vec ? launch(fwd16_kernel<T, DP, false, true, 2>, a, 64, st, 256, cfg.occ)
+                       : launch(fwd16_kernel<T, DP, false, false, 2>, a, 64, st, 256, cfg.occ);
         }
     }
     if (a.causal) {
-        return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256)
-                   : launch(fwd16_kernel<T, DP, true, false, 1>, a, 128, st, 256);
+        return vec ? launch(fwd16_kernel<T, DP, true, true, 1>, a, 128, st, 256, cfg.occ)
+                   : launch(fwd16_kernel<T, DP, true, false, 1>, a, 128, st, 256, cfg.occ);
     }
-    return vec ? launch(fwd16_kernel<T, DP, false, true, 1>, a, 128, st, 256)
-               : launch(fwd16_kernel<T, DP, false, false, 1>, a, 128, st, 256);
+    return vec ? launch(fwd16_kernel<T, DP, false, true, 1>, a, 128, st, 256, cfg.occ)
+               : launch(fwd16_kernel<T, DP, false, false, 1>, a, 128, st, 256, cfg.occ);
 }
 
 template <int DP, int BC>
@@ -1016,18 +1030,18 @@ static int launch32(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
     if constexpr (DP <= 96) {
         if (cfg.br == 64) {  // key split (d <= 96: checked by the caller)
             if (a.causal)
-                return vec ? launch(fwd32_kernel<DP, BC, true, true, 2>, a, 64, st, 256)
-                           : launch(fwd32_kernel<DP, BC, true, false, 2>, a, 64, st, 256);
-            return vec ? launch(fwd32_kernel<DP, BC, false, true, 2>, a, 64, st, 256)
-                       : launch(fwd32_kernel<DP, BC, false, false, 2>, a, 64, st, 256);
+                return vec ? launch(fwd32_kernel<DP, BC, true, true, 2>, a, 64, st, 256, cfg.occ)
+                           : launch(fwd32_kernel<DP, BC, true, false, 2>, a, 64, st, 256, cfg.occ);
+            return vec ? launch(fwd32_kernel<DP, BC, false, true, 2>, a, 64, st, 256, cfg.occ)
+                       : launch(fwd32_kernel<DP, BC, false, false, 2>, a, 64, st, 256, cfg.occ);
         }
     }
     if (a.causal) {
-        return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256)
-                   : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256);
+        return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256, cfg.occ)
+                   : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256, cfg.occ);
     }
-    return vec ? launch(fwd32_kernel<DP, BC, false, true, 1>, a, 128, st, 256)
-               : launch(fwd32_kernel<DP, BC, false, false, 1>, a, 128, st, 256);
+    return vec ? launch(fwd32_kernel<DP, BC, false, true, 1>, a, 128, st, 256, cfg.occ)
+               : launch(fwd32_kernel<DP, BC, false, false, 1>, a, 128, st, 256, cfg.occ);
 }
 
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream) {

@@ -22,6 +22,9 @@ struct FwdArgs {
     const int* cu_q;
     const int* cu_k;
     int64_t tq, tk;
+    // causal grids: workgroups an XCD takes per group of batch-head pairs in the
+    // heaviest-tile-first order (0: the kernel's own, its resident workgroups per XCD)
+    int slots;
 };
 
 // Tile configuration chosen by the selector.
@@ -30,6 +33,9 @@ struct TileConfig {
     int bc;     // keys per K/V tile
     int waves;  // waves per workgroup
     int dpad;   // head dimension the kernel is compiled for (multiple of 32, >= d)
+    // Knobs that leave every result bit-identical:
+    int occ;    // at most this many workgroups per CU (1..4), by reserving LDS; 0: no cap
+    int group;  // FwdArgs::slots for causal grids (8..1024); 0: the kernel's own
 };
 
 // Pure selection logic (no HIP calls). Returns 0 on success, 2 if no kernel fits.

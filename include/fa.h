@@ -140,13 +140,21 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  * (64, 64, 4), the two-way key split, when d <= 128. For fp32, (128, 64, 4) for d <= 96 and
  * (128, 32, 4) above, and (64, 64, 4) when d <= 96. Any other triple returns
  * FA_EUNSUPPORTED before any HIP call.
+ * Two knobs change only where and when workgroups run, never a result bit:
+ *  - occ (0..4): at most occ workgroups on one CU at a time, by reserving unused LDS
+ *    (160 KB / occ per workgroup); 0 = as many as the registers and LDS allow.
+ *  - group (0 or 8..1024): causal grids hand each XCD its batch-head pairs in groups, the
+ *    longest query tiles of a group first; group is the number of workgroups that such a
+ *    group should hold at least (0 = the workgroups the kernel keeps resident per XCD).
+ *    Non-causal grids ignore it.
+ * Values outside these ranges return FA_EUNSUPPORTED.
  * Everything else (arguments, ownership, errors) is as for fa_fwd; the result is the same
  * up to the order of the fp32 sums.
  */
 fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, float* lse,
                         int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                         float scale, int causal, fa_dtype dtype, int Br, int Bc, int waves,
-                        void* stream);
+                        int occ, int group, void* stream);
 
 /*
  * fa_tune_fwd -- measure every tile configuration that exists for this problem and keep
@@ -155,11 +163,14 @@ fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, fl
  * The pages' kernels pick tile sizes by hand and by search (page "Flash Attention Shared
  * Memory constraint", the group-size search; page "Add Fused Multi-Head Attention example":
  * its Python counterpart searches a space of hand-picked configurations). Here each
- * configuration fa_fwd_config accepts runs once untimed. The first of them then runs
+ * configuration fa_fwd_config accepts (with both knobs 0) runs once untimed. The first of them then runs
  * untimed for about 20 ms of GPU time, so that the GPU's clock has left its idle state.
  * After that, two rounds time `reps` launches (1..1000) of every configuration between two
- * HIP events on `stream`. Each configuration keeps its faster round, and the fastest
- * configuration is written to *Br, *Bc, *waves (each may be NULL) and remembered for this
+ * HIP events on `stream`. Each configuration keeps its faster round. From the fastest, the
+ * knobs of fa_fwd_config are then varied one at a time in two more rounds timed the same
+ * way: occ = 1 for 4-wave configurations, and for causal problems group = 16, 32, 64, 128;
+ * a variant replaces it only if faster. The result is written to *Br, *Bc, *waves, *occ,
+ * *group (each may be NULL) and remembered for this
  * exact problem (current device, dtype, B, H, Nq, Nk, d, causal). Later fa_fwd calls on the
  * same problem launch it instead of the built-in choice, as long as the buffers allow it
  * (a ping-pong choice needs 16-byte aligned buffers). The record holds up to 256 problems;
@@ -177,7 +188,7 @@ fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, fl
 fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                       float scale, int causal, fa_dtype dtype, int reps, void* stream,
-                      int* Br, int* Bc, int* waves);
+                      int* Br, int* Bc, int* waves, int* occ, int* group);
 
 /* Forgets every configuration fa_tune_fwd recorded (all devices). */
 void fa_tune_clear(void);

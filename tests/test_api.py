@@ -92,10 +92,10 @@ def test_varlen_unsupported(L, kw):
     assert call_varlen(L, **kw) == fa.FA_EUNSUPPORTED
 
 
-def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0.125):
+def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0.125, occ=0, group=0):
     Br, Bc, waves = cfg
     return L.fa_fwd_config(q, P, P, P, P, B, H, Nq, Nk, d, ctypes.c_float(scale), causal, dtype,
-                           Br, Bc, waves, None)
+                           Br, Bc, waves, occ, group, None)
 
 
 @pytest.mark.parametrize("cfg,kw", [
@@ -108,6 +108,9 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
     ((256, 64, 8), dict(d=60)),                # and for d % 8 == 0
     ((256, 64, 8), dict(q=P + 2)),             # and for 16-byte aligned rows
     ((512, 64, 16), dict()), ((128, 64, 8), dict()), ((0, 0, 0), dict()),
+    ((128, 64, 4), dict(occ=5)), ((128, 64, 4), dict(occ=-1)),       # knob ranges
+    ((128, 64, 4), dict(group=4)), ((128, 64, 4), dict(group=2048)),
+    ((128, 64, 4), dict(group=-8)),
 ])
 def test_fwd_config_unsupported(L, cfg, kw):
     """Configurations with no kernel are rejected before any HIP call."""
@@ -121,7 +124,7 @@ def test_fwd_config_invalid_arguments(L):
 
 
 def call_tune(L, reps=5, q=P, B=1, d=64, scale=0.125):
-    out = [ctypes.c_int(-1) for _ in range(3)]
+    out = [ctypes.c_int(-1) for _ in range(5)]
     rc = L.fa_tune_fwd(q, P, P, P, P, B, 1, 8, 8, d, ctypes.c_float(scale), 0, 2, reps, None,
                        *[ctypes.byref(x) for x in out])
     return rc, [x.value for x in out]
@@ -131,7 +134,7 @@ def call_tune(L, reps=5, q=P, B=1, d=64, scale=0.125):
                                 dict(scale=float("inf"))])
 def test_tune_invalid_arguments(L, kw):
     rc, out = call_tune(L, **kw)
-    assert rc == fa.FA_EINVAL and out == [-1, -1, -1]
+    assert rc == fa.FA_EINVAL and out == [-1] * 5
 
 
 def test_tune_clear_needs_no_gpu(L):

@@ -122,7 +122,9 @@ def test_tune_record_steers_fa_fwd(case):
     lt = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
     best = fa.fa_tune_fwd(q, k, v, ot, lt, scale, causal, reps=3)
     say(f"  {case}: built-in {rule}, tuned {best}")
-    assert best in admitted(dt, d, causal)
+    assert {k_: best[k_] for k_ in ("Br", "Bc", "waves")} in admitted(dt, d, causal)
+    assert best["occ"] in ((0, 1) if best["waves"] == 4 else (0,))
+    assert best["group"] in ((0, 16, 32, 64, 128) if causal else (0,))
     o1, l1 = run()
     o_b, l_b = run(best)
     assert torch.equal(o1, o_b) and torch.equal(l1, l_b)    # tuned: the recorded choice
@@ -130,3 +132,43 @@ def test_tune_record_steers_fa_fwd(case):
     fa.fa_tune_clear()
     o2, l2 = run()
     assert torch.equal(o2, o_r) and torch.equal(l2, l_r)    # cleared: built-in again
+
+
+KNOB_CASES = [
+    ("bf16", 1, 8, 1024, 1024, 128, True),   # 8 pairs: one per XCD, grouped causal order
+    ("f16", 2, 8, 1000, 1000, 64, True),     # 16 pairs, ragged last tile
+    ("f32", 1, 8, 700, 700, 64, True),
+    ("f16", 2, 4, 600, 900, 96, False),      # non-causal: group has no effect
+]
+KNOBS = [dict(occ=1), dict(occ=2), dict(group=8), dict(group=16), dict(group=128), dict(group=1024),
+         dict(occ=1, group=32)]
+
+
+@pytest.mark.parametrize("case", KNOB_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_knobs_leave_results_bit_identical(case):
+    """The occupancy cap and the causal dispatch group move workgroups, never arithmetic:
+    every admitted configuration with every knob setting equals its knob-free result bit for
+    bit, and the knob-free result matches the oracle. Outputs start as NaN, so a tile that no
+    workgroup writes under some group size fails."""
+    dt, B, H, Nq, Nk, d, causal = case
+    q, k, v = inputs(dt, B, H, Nq, Nk, d, 700 + Nq + d)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), scale, causal)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+
+    def run(cfg):
+        o = torch.full_like(qd, float("nan"))
+        lse = torch.full(qd.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+        fa.fa_fwd_config(qd, kd, vd, o, lse, scale, causal, cfg)
+        torch.cuda.synchronize()
+        return o, lse
+
+    for cfg in admitted(dt, d, causal):
+        o0, l0 = run(cfg)
+        oe = float(np.max(np.abs(o0.double().cpu().numpy() - o_ref)))
+        le = float(np.max(np.abs(l0.double().cpu().numpy() - l_ref)))
+        say(f"  {case} {cfg}: max|dO| {oe:.3e} max|dL| {le:.3e}")
+        assert oe <= TOL_O[dt] and le <= TOL_L, (case, cfg)
+        for knob in KNOBS:
+            o1, l1 = run({**cfg, **knob})
+            assert torch.equal(o0, o1) and torch.equal(l0, l1), (case, cfg, knob)
