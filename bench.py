@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67533826, "kernel_sha": "f3b5a45c52cdca42"},
+    "pages_f32": {"bytes": 67533898, "kernel_sha": "50e6b74f8c3746a4"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269682055, "kernel_sha": "f3b5a45c52cdca42"},
+    "d128_bf16": {"bytes": 269681892, "kernel_sha": "50e6b74f8c3746a4"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 305405851, "kernel_sha": "f3b5a45c52cdca42"},
+    "d128_bf16_causal": {"bytes": 391316387, "kernel_sha": "50e6b74f8c3746a4"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78285277, "kernel_sha": "f3b5a45c52cdca42"},
+    "long_causal_bf16": {"bytes": 78276346, "kernel_sha": "50e6b74f8c3746a4"},
 }
 
 

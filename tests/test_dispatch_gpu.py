@@ -40,7 +40,7 @@ def _lib():
 
 # (dtype, B, H, N, d, kernel waves the selector must pick): 40 pairs = 5 per XCD
 CASES = [
-    ("bf16", 5, 8, 2560, 128, 8),  # ping-pong kernel: 10 query tiles of 256, groups of 4 pairs
+    ("bf16", 5, 8, 4352, 128, 8),  # ping-pong kernel: 17 query tiles of 256, groups of 4 pairs
     ("bf16", 5, 8, 2048, 64, 4),   # 4-wave kernel (causal, <= 4096 keys): 16 tiles, groups of 4
     ("f16", 5, 8, 2048, 36, 4),    # 4-wave kernel (d % 8 != 0): 16 tiles of 128, groups of 4
     ("f32", 5, 8, 2048, 64, 4),    # fp32 kernel: 16 tiles of 128, groups of 4
