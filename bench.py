@@ -173,7 +173,8 @@ def time_varlen(fa, torch, causal, steps, warmup):
 
 def tune_table(fa, torch, steps):
     """fa_tune_fwd on a few problems off the headline set: the built-in tile choice and the
-    tuned one, each timed over `steps` launches with HIP events (the record is cleared after)."""
+    tuned one, each timed over `steps` launches with HIP events in two alternating rounds,
+    keeping each one's faster round (the record is cleared after)."""
     from exact_attention_58_amd.workloads import Workload, make_inputs
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -191,17 +192,18 @@ def tune_table(fa, torch, steps):
         rule = {x: rule[x] for x in ("Br", "Bc", "waves")}
         best = fa.fa_tune_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, reps=max(3, steps // 5))
         times = {}
-        for name, cfg in (("built_in", rule), ("tuned", best)):
-            warm_up(torch, lambda: fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream),
-                    2, stream)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(steps):
-                fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream)
-            e1.record(stream)
-            torch.cuda.synchronize(dev)
-            times[name] = e0.elapsed_time(e1) / steps
+        for _ in range(2):
+            for name, cfg in (("built_in", rule), ("tuned", best)):
+                warm_up(torch, lambda: fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream),
+                        2, stream)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(steps):
+                    fa.fa_fwd_config(q, k, v, o, lse, w.softmax_scale, w.causal, cfg, stream)
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                times[name] = min(times.get(name, float("inf")), e0.elapsed_time(e1) / steps)
         out.append({"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                     "dtype": w.dtype, "causal": w.causal, "built_in": rule, "tuned": best,
                     "built_in_ms": round(times["built_in"], 4), "tuned_ms": round(times["tuned"], 4),

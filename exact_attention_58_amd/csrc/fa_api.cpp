@@ -7,6 +7,7 @@
 // Attention Shared Memory constraint", the group-size search).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -386,11 +387,29 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
             knob[n_knob] = best;
             knob[n_knob++].occ = 1;
         }
-        if (causal)
+        // group sizes only where the dispatch order changes: causal grids whose pairs split
+        // evenly over the 8 XCDs, and a number of pairs per group not tried yet (the
+        // built-in slots are those the kernels pass: 32 for the 16-bit 4-wave kernel above
+        // d = 128, else 64)
+        if (causal && B * H % 8 == 0) {
+            const int64_t per = B * H / 8, n_tiles = (Nq + best.br - 1) / best.br;
+            auto pairs_per_group = [&](int slots) {
+                return std::min<int64_t>(per, (slots + n_tiles - 1) / n_tiles);
+            };
+            const int builtin = (dtype != FA_F32 && best.waves == 4 && dpad > 128) ? 32 : 64;
+            int64_t seen[5];
+            int n_seen = 0;
+            seen[n_seen++] = pairs_per_group(builtin);
             for (int g : {16, 32, 64, 128}) {
+                const int64_t G = pairs_per_group(g);
+                bool dup = false;
+                for (int j = 0; j < n_seen; ++j) dup = dup || seen[j] == G;
+                if (dup) continue;
+                seen[n_seen++] = G;
                 knob[n_knob] = best;
                 knob[n_knob++].group = g;
             }
+        }
     }
     float knob_ms[kKnobs] = {};
     for (int round = 0; round < 2 && result == FA_OK && n_knob > 1; ++round)

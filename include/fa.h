@@ -168,8 +168,9 @@ fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, fl
  * After that, two rounds time `reps` launches (1..1000) of every configuration between two
  * HIP events on `stream`. Each configuration keeps its faster round. From the fastest, the
  * knobs of fa_fwd_config are then varied one at a time in two more rounds timed the same
- * way: occ = 1 for 4-wave configurations, and for causal problems group = 16, 32, 64, 128;
- * a variant replaces it only if faster. The result is written to *Br, *Bc, *waves, *occ,
+ * way: occ = 1 for 4-wave configurations, and for causal problems whose B*H pairs split
+ * evenly over the 8 XCDs those of group = 16, 32, 64, 128 that put a different number of
+ * pairs in a group than the built-in order does; a variant replaces it only if faster. The result is written to *Br, *Bc, *waves, *occ,
  * *group (each may be NULL) and remembered for this
  * exact problem (current device, dtype, B, H, Nq, Nk, d, causal). Later fa_fwd calls on the
  * same problem launch it instead of the built-in choice, as long as the buffers allow it
