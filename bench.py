@@ -37,13 +37,13 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67533898, "kernel_sha": "50e6b74f8c3746a4"},
+    "pages_f32": {"bytes": 67533834, "kernel_sha": "251466a61bf0d475"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269681892, "kernel_sha": "50e6b74f8c3746a4"},
+    "d128_bf16": {"bytes": 269681948, "kernel_sha": "251466a61bf0d475"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 391316387, "kernel_sha": "50e6b74f8c3746a4"},
+    "d128_bf16_causal": {"bytes": 390177888, "kernel_sha": "251466a61bf0d475"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78276346, "kernel_sha": "50e6b74f8c3746a4"},
+    "long_causal_bf16": {"bytes": 78285172, "kernel_sha": "251466a61bf0d475"},
 }
 
 

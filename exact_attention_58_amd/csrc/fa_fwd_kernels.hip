@@ -82,7 +82,8 @@ struct TileId {
 };
 // slots: the workgroups one group of pairs should hold at least. The 4-wave kernels pass what
 // an XCD holds at once (32 CUs x 2); the ping-pong kernel passes twice its 32 resident ones,
-// which measured about 2% faster on causal grids of 2 or more pairs per XCD.
+// which measured about 2% faster on dense causal grids of 2 or more pairs per XCD (packed
+// batches: 32).
 __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles, int slots) {
     const int i = blockIdx.x;
     if (a.slots > 0) slots = a.slots;
@@ -487,7 +488,9 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int grp = wave / WPG, wig = wave % WPG;
 
-    const TileId wt = tile_of(a, n_qtiles, 64);
+    // packed batches keep groups of 32 workgroups: with 64 the causal bench batch (16
+    // sequences of 533..3973) ran 10-14% slower, its groups then mixing sequences
+    const TileId wt = tile_of(a, n_qtiles, a.cu_q != nullptr ? 32 : 64);
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;
