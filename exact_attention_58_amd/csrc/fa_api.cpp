@@ -136,7 +136,15 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // causal grids (measured below 2 per CU: B1 H20 N2048 d64 265 -> 221 us, causal
         // B1 H40 N1024 97 -> 74 us). d <= 96: at d = 128 the split's two staged tiles no
         // longer fit the registers.
-        if (c.dpad <= 96 && (Nq + 127) / 128 * B * H < 2 * num_cus && Nk > 2 * c.bc) c.br = 64;
+        const int64_t wgs128 = (Nq + 127) / 128 * B * H;
+        if (c.dpad <= 96 && wgs128 < (causal ? 4 : 2) * num_cus && Nk > 2 * c.bc) c.br = 64;
+        // Causal grids (tuned on MI355X): the split up to four workgroups per CU, in dispatch
+        // groups of 128 (B1 H16 N4096 d64: 402 -> 294 us; B1 H64 N1024: 107 -> 91 us; B1 H40
+        // N1024 d64 split 71.6 -> 63.2 us with groups of 128), and above d = 96 one workgroup
+        // per CU (B1 H64 N1024 d128: 205 -> 174 us; B1 H16 N4096: 786 -> 609 us). Neither
+        // knob changes a result bit.
+        if (causal && c.br == 64) c.group = 128;
+        if (causal && c.dpad > 96) c.occ = 1;
     } else {
         c.bc = 64;
         // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte
@@ -156,7 +164,10 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         const int64_t pp_min_keys = !causal ? 512 : d <= 64 ? 4096 : 2048;
         if (d > 128) {
             // head dims past 128: the 4-wave kernel, one wave per SIMD
-        } else if (aligned && d % 8 == 0 && d > 32 && wgs256 >= num_cus && Nk > pp_min_keys) {
+        } else if (aligned && d % 8 == 0 && d > 32 && wgs256 * 8 >= (int64_t)num_cus * (causal ? 8 : 5) &&
+                   Nk > pp_min_keys) {
+            // non-causal grids keep the ping-pong kernel down to 5/8 of a workgroup per CU
+            // (B1 H20 N2048 d64: 46.5 -> 39.7 us; B1 H56 N1024 d128: 41.2 -> 38.1 us)
             c.waves = 8;
             c.br = 256;
         } else if (c.dpad <= 128 && (wgs128 < num_cus || (causal && wgs128 < 2 * num_cus)) &&

@@ -217,7 +217,10 @@ def test_select_config_grid_fill(dtype):
     assert small_causal["waves"] == 4 and small_causal["Br"] == 64  # causal grids split too
     # between one and two 128-row workgroups per CU: causal grids split, non-causal do not
     assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["Br"] == 64
-    assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
+    # non-causal: the ping-pong kernel down to 5/8 of a 256-row workgroup per CU
+    assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 256
+    assert fa.fa_select_config(dtype, 1, 16, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["waves"] == 4
     assert fa.fa_select_config(dtype, 1, 40, 2048, 2048, 64, True, num_cus=256)["Br"] == 128
     small_d128 = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 128, False, num_cus=256)
     assert small_d128["Br"] == 64  # the key split reaches d = 128 for 16-bit inputs
@@ -256,6 +259,9 @@ def test_select_config_fp32_key_split():
     # up to two 128-row workgroups per CU (fp32, causal or not)
     assert fa.fa_select_config("f32", 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 1, 40, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
+    # causal fp32 splits up to four per CU
+    assert fa.fa_select_config("f32", 1, 16, 4096, 4096, 64, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 1, 64, 4096, 4096, 64, True, num_cus=256)["Br"] == 128
     assert fa.fa_select_config("f32", 1, 8, 1024, 128, 64, False, num_cus=256)["Br"] == 128
 
 
