@@ -234,7 +234,9 @@ const char* fa_status_str(fa_status s);
  * sizes; pure host logic, no HIP call. Writes the query rows per workgroup
  * (*Br), the keys per K/V tile (*Bc), the waves per workgroup (*waves) and
  * the padded head dimension the kernel is compiled for (*dpad). Any output
- * pointer may be NULL. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
+ * pointer may be NULL. The scheduling knobs of fa_fwd_config that the built-in
+ * rules set (one workgroup per CU and dispatch groups of 128 for some causal
+ * fp32 problems) are not reported; they change no result bit. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
  * `num_cus` is the device's compute-unit count (256 on MI355X); it only
  * affects the query-tile height: grids of fewer 128-row workgroups than CUs
  * (than two per CU for causal grids and for fp32) take the two-way key split. Key
