@@ -165,6 +165,20 @@ def test_key_split_up_to_two_workgroups_per_cu(dt, causal):
     full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} split B1 H20 N2048 causal={causal}")
 
 
+@pytest.mark.parametrize("dt,B,H,N,d,causal,waves,br", [
+    ("f32", 1, 16, 4096, 128, True, 4, 128),   # one workgroup per CU (reserved LDS)
+    ("f32", 1, 16, 4096, 64, True, 4, 64),     # causal split at 4 workgroups per CU, groups of 128
+    ("bf16", 2, 12, 2048, 96, False, 8, 256),  # ping-pong grid of 192 workgroups (3/4 per CU)
+])
+def test_tuned_rule_shapes(dt, B, H, N, d, causal, waves, br):
+    """Built-in choices that came from timing the scheduling knobs, at the sizes measured:
+    every row against the oracle."""
+    cfg = fa.fa_select_config(dt, B, H, N, N, d, causal)
+    assert (cfg["waves"], cfg["Br"]) == (waves, br), cfg
+    q, k, v = (make_random((B, H, N, d), dt, 950 + i) for i in range(3))
+    full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} B{B} H{H} N{N} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_increasing_scores_force_rescales(dt):
     """Scores that grow along the keys: every tile raises the row max by more than the
