@@ -84,11 +84,33 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def time_workload(fa, torch, w, steps, warmup, inputs=None):
-    """Runs `steps` back-to-back fa_fwd calls on torch's current stream, after warm_up.
+def launch_stats(torch, call, n, stream):
+    """n more launches, each between its own pair of HIP events on the launch stream; returns
+    the median, mean and 10th/90th percentiles of the launch durations (ms)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    pick = lambda f: t[min(n - 1, int(round(f * (n - 1))))]
+    return {"launches": n, "median_ms": round(pick(0.5), 5), "mean_ms": round(sum(t) / n, 5),
+            "p10_ms": round(pick(0.1), 5), "p90_ms": round(pick(0.9), 5)}
 
-    Returns (wall ms per step, average launch duration in ms from HIP events recorded on
-    the launch stream around the timed region, warm-up calls made)."""
+
+def per_launch_count(w, steps) -> int:
+    """Launches timed one by one: at least 30, and at least 200 for workloads under a GFLOP."""
+    return max(steps, 200 if w.flops < 1e9 else 30)
+
+
+def time_workload(fa, torch, w, steps, warmup, inputs=None, keep_outputs=False):
+    """Runs `steps` back-to-back fa_fwd calls on torch's current stream, after warm_up, then
+    per_launch_count() more calls timed one by one.
+
+    Returns (wall ms per step, average launch duration in ms from HIP events recorded on the
+    launch stream around the timed region, warm-up calls made, per-launch statistics, and the
+    outputs (o, lse) on the host when keep_outputs)."""
     from exact_attention_58_amd.workloads import make_inputs
     dev = torch.device("cuda:0")
     if inputs is None:
@@ -98,20 +120,23 @@ def time_workload(fa, torch, w, steps, warmup, inputs=None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    n_warm = warm_up(torch, lambda: fa.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream),
-                     warmup, stream)
+    call = lambda: fa.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    n_warm = warm_up(torch, call, warmup, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(steps):
-        fa.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+        call()
     e1.record(stream)
     torch.cuda.synchronize(dev)
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ev_ms = e0.elapsed_time(e1) / steps
+    stats = launch_stats(torch, call, per_launch_count(w, steps), stream)
+    outs = (o.cpu(), lse.cpu()) if keep_outputs else None
     del o, lse
-    return wall_ms, ev_ms, n_warm
+    return wall_ms, ev_ms, n_warm, stats, outs
 
 
 def time_backward(fa, torch, w, steps, warmup):
@@ -276,32 +301,41 @@ def hbm_sweep(fa, torch, steps):
     return out, round(copy_gbs, 1)
 
 
-def cpu_baseline(w, target_s: float = 15.0):
-    """The fp64 oracle as it stands, on the host cores, on a bounded row sample."""
+def oracle_leg(w, outs):
+    """CPU-baseline leg: the fp64 oracle as it stands, on the host cores, over every row of the
+    workload (outside every timed region). Reports its wall time and rate, and the max-abs
+    error of the GPU's O and L (the launch the benchmark timed) with where it occurs."""
     import numpy as np
 
     import oracle
     from exact_attention_58_amd.workloads import make_inputs
     q, k, v = make_inputs(w)
-    qd, kd, vd = q.double(), k.double(), v.double()
     threads = oracle.default_threads()
-    total_rows = w.B * w.H * w.Nq
-    per_row = 4.0 * w.Nk * w.d  # non-causal rows; the headline workload is non-causal
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.attention_fwd(q.double(), k.double(), v.double(), w.softmax_scale, w.causal,
+                                        threads=threads)
+    dt = time.perf_counter() - t0
+    rep = {"rows": w.B * w.H * w.Nq, "wall_s": round(dt, 2), "cores": threads,
+           "tflops": round(w.flops / dt / 1e12, 5)}
+    if outs is not None:
+        o, lse = outs
+        do = np.abs(o.double().numpy() - o_ref)
+        dl = np.abs(lse.double().numpy() - l_ref)
+        io, il = np.unravel_index(np.argmax(do), do.shape), np.unravel_index(np.argmax(dl), dl.shape)
+        tol_o = 1e-4 if w.dtype == "f32" else 2e-2
+        rep.update({"max_abs_err_O": float(do[io]), "at_O_bhic": [int(x) for x in io],
+                    "ref_O_there": round(float(o_ref[io]), 4),
+                    "max_abs_err_L": float(dl[il]), "at_L_bhi": [int(x) for x in il],
+                    "tol_O": tol_o, "tol_L": 1e-3,
+                    "within_tol": bool(do[io] <= tol_o and dl[il] <= 1e-3)})
+    return rep
 
-    def run(nrows):
-        rows = np.linspace(0, total_rows - 1, nrows).round().astype(np.int64)
-        t0 = time.perf_counter()
-        oracle.attention_fwd(qd, kd, vd, w.softmax_scale, w.causal, rows=rows, threads=threads)
-        return time.perf_counter() - t0, len(rows)
 
-    dt, n = run(max(threads * 8, 256))
-    rate = n / dt
-    n2 = int(min(total_rows, max(n, rate * target_s)))
-    dt, n = run(n2)
-    flops = n * per_row
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {total_rows} query rows of {w.name} (evenly spaced over all heads), "
-                      f"{dt:.1f} s wall, fp64"}
+def cpu_baseline(w, rep):
+    """The headline's CPU baseline line from its oracle leg (all rows of the workload)."""
+    return {"value": rep["tflops"], "unit": "TFLOP/s", "cores": rep["cores"], "kind": "oracle",
+            "sample": f"all {rep['rows']} query rows of {w.name} (the whole workload), "
+                      f"{rep['wall_s']:.1f} s wall on {rep['cores']} threads, fp64"}
 
 
 def main():
@@ -344,11 +378,16 @@ def main():
     props = torch.cuda.get_device_properties(0)
 
     w = WORKLOADS[args.workload]
+    with_oracle = not args.quick and not args.no_cpu
     log(f"headline {w.name}: {args.warmup} warmup + {args.steps} timed steps")
     torch.cuda.synchronize()
-    wall_ms, ev_ms, n_warm = time_workload(fa, torch, w, args.steps, args.warmup)
+    wall_ms, ev_ms, n_warm, stats, outs = time_workload(fa, torch, w, args.steps, args.warmup,
+                                                        keep_outputs=with_oracle)
     tflops = w.flops / (wall_ms * 1e-3) / 1e12
-    log(f"  {w.name}: {wall_ms:.3f} ms/step wall, {ev_ms:.3f} ms/launch (events), {tflops:.1f} TFLOP/s")
+    log(f"  {w.name}: dispatches {n_warm}..{n_warm + args.steps - 1} of its kernel are the timed region; "
+        f"{wall_ms:.3f} ms/step wall, {ev_ms:.4f} ms/launch (events), {tflops:.1f} TFLOP/s; "
+        f"one by one: median {stats['median_ms']} ms over {stats['launches']}")
+    outputs = {w.name: outs}
 
     also = []
     sweep, copy_gbs, tuned = None, None, None
@@ -357,12 +396,17 @@ def main():
             if name == w.name:
                 continue
             steps = max(5, min(args.steps, 200 if ow.flops < 1e9 else args.steps))
-            wm, em, _ = time_workload(fa, torch, ow, steps, args.warmup)
+            wm, em, _, st, oo = time_workload(fa, torch, ow, steps, args.warmup, keep_outputs=with_oracle)
+            outputs[name] = oo
             r = roofline_for(ow, em, sha)
             also.append({"workload": name, "B": ow.B, "H": ow.H, "Nq": ow.Nq, "Nk": ow.Nk, "d": ow.d,
-                         "dtype": ow.dtype, "causal": ow.causal, "ms_per_step": round(wm, 4),
-                         "tflops": round(ow.flops / (wm * 1e-3) / 1e12, 2), "roofline": r})
-            log(f"  {name}: {wm:.3f} ms/step, {r['achieved']} TFLOP/s kernel, {100 * r['frac']:.1f}% of {ow.dtype} peak")
+                         "dtype": ow.dtype, "causal": ow.causal, "steps": steps, "ms_per_step": round(wm, 4),
+                         "tflops": round(ow.flops / (wm * 1e-3) / 1e12, 2), "kernel_ms_mean": round(em, 5),
+                         "per_launch": st,
+                         "tflops_at_median": round(ow.flops / (st["median_ms"] * 1e-3) / 1e12, 2),
+                         "roofline": r})
+            log(f"  {name}: {wm:.4f} ms/step, {r['achieved']} TFLOP/s kernel, {100 * r['frac']:.1f}% of "
+                f"{ow.dtype} peak; median {st['median_ms']} ms over {st['launches']} launches")
         # backward (FLOP convention: 2.5 x the forward's, i.e. five products of the forward's
         # size; this implementation recomputes S and dP in both tile kernels)
         for name in ("d128_bf16", "d128_bf16_causal", "long_causal_bf16"):
@@ -395,11 +439,19 @@ def main():
             log(f"  short N={s['N']}: {s['GB_per_s']} GB/s ({100 * s['hbm_frac']:.1f}% of 8 TB/s)")
         log(f"  2 GiB device copy: {copy_gbs} GB/s")
 
-    cpu = None
-    if not args.quick and not args.no_cpu:
-        log("cpu baseline (fp64 oracle)...")
-        cpu = cpu_baseline(w)
-        log(f"  {cpu}")
+    cpu, head_oracle = None, None
+    if with_oracle:
+        # CPU-baseline leg: the oracle over every row of every workload, outside the timed
+        # regions; its time is the baseline, its comparison the error report per workload
+        for name, oo in outputs.items():
+            rep = oracle_leg(WORKLOADS[name], oo)
+            log(f"  oracle {name}: {rep}")
+            if name == w.name:
+                cpu = cpu_baseline(w, rep)
+                head_oracle = rep
+            else:
+                next(a for a in also if a["workload"] == name)["oracle"] = rep
+        del outputs
 
     line = {
         "metric": "attention fwd TFLOP/s and % of MI355X dtype peak (B4 H4 N4096 d64/d128)",
@@ -421,8 +473,11 @@ def main():
                    "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
                    "global_batch": w.B, "seq_len": w.Nq, "parallelism": "single GPU"},
         "pct_of_peak": round(100 * tflops / PEAK_TFLOPS[w.dtype], 2),
+        "kernel_ms_mean": round(ev_ms, 5),
+        "per_launch": stats,
         "roofline": roofline_for(w, ev_ms, sha),
         "cpu_baseline": cpu,
+        "oracle": head_oracle,
         "also": also,
         "hbm_sweep": {"runs": sweep, "device_copy_GB_per_s": copy_gbs} if sweep else None,
         "autotune": tuned,

@@ -5,7 +5,7 @@ behind the C ABI declared in include/fa.h. PyTorch is used for device memory and
 streams. There is no fallback: if the library is missing, the calls raise.
 
     fa_fwd(q, k, v, o, lse, scale, causal, stream=None)   # C-ABI fa_fwd on torch tensors
-    fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict
+    fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus=256) -> dict   # num_cus=None: current device
     fa_status_str(code) -> str
     attention(q, k, v, scale=None, causal=False) -> (o, lse)  # allocates o and lse
     fa_fwd_config(q, k, v, o, lse, scale, causal, cfg, stream=None)   # cfg: {"Br","Bc","waves"}
@@ -28,7 +28,9 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear", "fa_bwd", "fa_status_str", "fa_select_config", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear", "fa_bwd",
+            "fa_status_str", "fa_select_config", "fa_select_config_cus", "fa_version")
+ABI_VERSION = 2
 DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
 
 _lock = threading.Lock()
@@ -86,10 +88,15 @@ def lib():
             L.fa_status_str.argtypes = [ctypes.c_int]
             ip = ctypes.POINTER(ctypes.c_int)
             L.fa_select_config.restype = ctypes.c_int
-            L.fa_select_config.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int,
-                                           ctypes.c_int, ip, ip, ip, ip]
+            L.fa_select_config.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ip, ip, ip]
+            L.fa_select_config_cus.restype = ctypes.c_int
+            L.fa_select_config_cus.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int,
+                                               ctypes.c_int, ip, ip, ip, ip]
             L.fa_version.restype = ctypes.c_int
             L.fa_version.argtypes = []
+            if L.fa_version() < ABI_VERSION:
+                raise RuntimeError(f"{LIB_PATH} is interface version {L.fa_version()}, older than "
+                                   f"{ABI_VERSION}: rebuild it with `python -m exact_attention_58_amd.build`")
             _lib = L
     return _lib
 
@@ -98,13 +105,23 @@ def fa_status_str(code: int) -> str:
     return lib().fa_status_str(int(code)).decode()
 
 
-def fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus: int = 256) -> dict:
+def fa_select_config(dtype, B, H, Nq, Nk, d, causal, num_cus: int | None = 256) -> dict:
+    """The tile configuration fa_fwd would launch: {"Br", "Bc", "waves"} (+ "dpad" when
+    num_cus is given). num_cus=None asks the C-ABI fa_select_config for the current device;
+    a number calls the pure fa_select_config_cus with that compute-unit count."""
     dt = DTYPE_NAMES.get(dtype, dtype)
+    if num_cus is None:
+        out = [ctypes.c_int(0) for _ in range(3)]
+        rc = lib().fa_select_config(int(dt), B, H, Nq, Nk, d, int(bool(causal)),
+                                    *[ctypes.byref(x) for x in out])
+        if rc != FA_OK:
+            raise FaError(rc, "fa_select_config")
+        return dict(zip(("Br", "Bc", "waves"), (x.value for x in out)))
     out = [ctypes.c_int(0) for _ in range(4)]
-    rc = lib().fa_select_config(int(dt), B, H, Nq, Nk, d, int(bool(causal)), int(num_cus),
-                                *[ctypes.byref(x) for x in out])
+    rc = lib().fa_select_config_cus(int(dt), B, H, Nq, Nk, d, int(bool(causal)), int(num_cus),
+                                    *[ctypes.byref(x) for x in out])
     if rc != FA_OK:
-        raise FaError(rc, "fa_select_config")
+        raise FaError(rc, "fa_select_config_cus")
     return dict(zip(("Br", "Bc", "waves", "dpad"), (x.value for x in out)))
 
 
@@ -284,12 +301,12 @@ def attention_varlen(q, k, v, cu_q, cu_k, max_q: int | None = None, max_k: int |
     return o, lse
 
 
-def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale: float, causal: bool, stream=None) -> None:
-    """Calls the C-ABI fa_bwd on contiguous device tensors (gradients and the fp32 [B,H,Nq]
-    workspace `delta` preallocated)."""
+def _check_bwd(q, k, v, o, lse, do, dq, dk, dv, delta):
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do),
-                    ("dq", dq), ("dk", dk), ("dv", dv), ("delta", delta)):
+    named = [("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do), ("dq", dq), ("dk", dk), ("dv", dv)]
+    if delta is not None:
+        named.append(("delta", delta))
+    for name, t in named:
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
@@ -300,22 +317,29 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale: float, causal: bool, s
     Nk = k.shape[2]
     if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    for name, t, shape in (("o", o, (B, H, Nq, d)), ("do", do, (B, H, Nq, d)), ("dq", dq, (B, H, Nq, d)),
-                           ("dk", dk, (B, H, Nk, d)), ("dv", dv, (B, H, Nk, d)),
-                           ("lse", lse, (B, H, Nq)), ("delta", delta, (B, H, Nq))):
+    shapes = [("o", o, (B, H, Nq, d)), ("do", do, (B, H, Nq, d)), ("dq", dq, (B, H, Nq, d)),
+              ("dk", dk, (B, H, Nk, d)), ("dv", dv, (B, H, Nk, d)), ("lse", lse, (B, H, Nq))]
+    if delta is not None:
+        shapes.append(("delta", delta, (B, H, Nq)))
+    for name, t, shape in shapes:
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {list(shape)}")
     if not all(t.dtype == q.dtype for t in (k, v, o, do, dq, dk, dv)):
         raise TypeError("q, k, v, o, do, dq, dk, dv must share one dtype")
-    if lse.dtype != torch.float32 or delta.dtype != torch.float32:
+    if lse.dtype != torch.float32 or (delta is not None and delta.dtype != torch.float32):
         raise TypeError("lse and delta must be float32")
-    dev = q.device
-    if any(t.device != dev for t in (k, v, o, lse, do, dq, dk, dv, delta)):
+    if any(t.device != q.device for _, t in named):
         raise ValueError("all tensors must be on one device")
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    with torch.cuda.device(dev):
+    return B, H, Nq, Nk, d
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale: float, causal: bool, stream=None) -> None:
+    """Calls the C-ABI fa_bwd on contiguous device tensors (gradients and the fp32 [B,H,Nq]
+    workspace `delta` preallocated)."""
+    import torch
+    B, H, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, delta)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
         rc = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                           B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q), handle)

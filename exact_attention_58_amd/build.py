@@ -25,23 +25,43 @@ FLAGS = [
 ]
 
 
-def build(resource_usage: bool = False, verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS]
-    if resource_usage:
-        cmd.append("-Rpass-analysis=kernel-resource-usage")
-    cmd += ["-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    """Compiles each source to an object (in parallel), then links the shared library."""
+    tag = f".tmp{os.getpid()}"
+    objs = [os.path.join(CSRC, os.path.basename(src) + tag + ".o") for src in SOURCES]
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
     # hipcc's host pass does not know the packed-fp32 target feature; that warning is noise
     noise = ("packed-fp32-ops", "is not a recognized feature for this target")
-    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if not any(n in l for n in noise))
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
-    if msg.strip() and (verbose or resource_usage):
-        print(msg)
-    os.replace(tmp, LIB)
+    out = []
+    try:
+        procs = [_run([HIPCC, *FLAGS, *extra, "-c", "-o", obj, src], verbose) for src, obj in zip(SOURCES, objs)]
+        failed = []
+        for src, p in zip(SOURCES, procs):
+            text = p.communicate()[0]
+            out.append(text)
+            if p.returncode != 0:
+                failed.append(src)
+        msg = "\n".join(l for l in "\n".join(out).splitlines() if not any(n in l for n in noise))
+        if failed:
+            raise RuntimeError(f"hipcc failed on {failed}:\n{msg}")
+        if msg.strip() and (verbose or resource_usage):
+            print(msg)
+        tmp = LIB + tag
+        link = _run([HIPCC, *FLAGS, "-o", tmp, *objs], verbose)
+        text = link.communicate()[0]
+        if link.returncode != 0:
+            raise RuntimeError(f"link failed ({link.returncode}):\n{text}")
+        os.replace(tmp, LIB)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return LIB
 
 

@@ -239,6 +239,46 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     return launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
+// Body of fa_bwd: argument checks (before any HIP call), then the launches with `delta` as
+// the row-term workspace.
+fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
+                  int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
+                  void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_EINVAL;
+    if (!std::isfinite(scale)) return FA_EINVAL;
+    fa_status st = check_args(dtype, B, H, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    const uintptr_t all = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+                          (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
+    const int esz = dtype == FA_F32 ? 4 : 2;
+    if (all % esz != 0 || (uintptr_t)lse % 4 != 0) return FA_EINVAL;
+    // the backward kernels exist for the 16-bit types on 16-byte rows, d <= 128, only
+    if (dtype == FA_F32 || d % 8 != 0 || d > kMaxDim32 || all % 16 != 0) return FA_EUNSUPPORTED;
+    BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.delta = delta;
+    a.B = (int)B;
+    a.H = (int)H;
+    a.Nq = (int)Nq;
+    a.Nk = (int)Nk;
+    a.d = (int)d;
+    a.scale = scale;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+    a.causal = causal ? 1 : 0;
+    a.dtype = (int)dtype;
+    const int dpad = (int)((d + 31) / 32) * 32;
+    return launch_bwd(a, dpad, stream) == 0 ? FA_OK : FA_ELAUNCH;
+}
+
 }  // namespace
 
 }  // namespace fa
@@ -255,10 +295,10 @@ const char* fa_status_str(fa_status s) {
     return "unknown fa_status";
 }
 
-int fa_version(void) { return 1; }
+int fa_version(void) { return 2; }
 
-fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                           int causal, int num_cus, int* Br, int* Bc, int* waves, int* dpad) {
+fa_status fa_select_config_cus(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                               int causal, int num_cus, int* Br, int* Bc, int* waves, int* dpad) {
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
     fa::TileConfig cfg;
@@ -269,6 +309,14 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
     if (waves) *waves = cfg.waves;
     if (dpad) *dpad = cfg.dpad;
     return FA_OK;
+}
+
+fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                           int causal, int* Br, int* Bc, int* waves) {
+    // the current device's compute-unit count (cached); MI355X's 256 when no device is visible
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) cus = fa::dev_num_cus(dev);
+    return fa_select_config_cus(dtype, B, H, Nq, Nk, d, causal, cus, Br, Bc, waves, nullptr);
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -465,37 +513,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
                  int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
                  void* stream) {
-    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_EINVAL;
-    if (!std::isfinite(scale)) return FA_EINVAL;
-    fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
-    if (st != FA_OK) return st;
-    const uintptr_t all16 = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
-                            (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
-    if (all16 % 2 != 0 || (uintptr_t)lse % 4 != 0 || (uintptr_t)delta % 4 != 0) return FA_EINVAL;
-    // the backward kernels exist for the 16-bit types on 16-byte rows, d <= 128, only
-    if (dtype == FA_F32 || d % 8 != 0 || d > fa::kMaxDim32 || all16 % 16 != 0) return FA_EUNSUPPORTED;
-    fa::BwdArgs a;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.dout = dout;
-    a.lse = lse;
-    a.dq = dq;
-    a.dk = dk;
-    a.dv = dv;
-    a.delta = delta;
-    a.B = (int)B;
-    a.H = (int)H;
-    a.Nq = (int)Nq;
-    a.Nk = (int)Nk;
-    a.d = (int)d;
-    a.scale = scale;
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
-    a.causal = causal ? 1 : 0;
-    a.dtype = (int)dtype;
-    const int dpad = (int)((d + 31) / 32) * 32;
-    return fa::launch_bwd(a, dpad, stream) == 0 ? FA_OK : FA_ELAUNCH;
+    if (!delta || (uintptr_t)delta % 4 != 0) return FA_EINVAL;
+    return fa::run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype,
+                       stream);
 }
 
 }  // extern "C"

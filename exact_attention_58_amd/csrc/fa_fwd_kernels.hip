@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -989,17 +990,41 @@ constexpr size_t kLdsPerCu = 160 * 1024;
 // occ > 0 caps the workgroups a CU holds at once: each launch also reserves unused dynamic
 // LDS so that one workgroup's share is kLdsPerCu / occ (no reservation when the kernel's
 // own LDS already exceeds that share).
+// Static LDS bytes of a kernel, asked of the runtime once per kernel (the code object is the
+// same on every gfx950 device) and remembered.
+static hipError_t static_lds(const void* fn, size_t* out) {
+    struct Entry {
+        const void* fn;
+        size_t lds;
+    };
+    static std::mutex mu;
+    static Entry cache[128];
+    static int used = 0;
+    std::lock_guard<std::mutex> lk(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].fn == fn) {
+            *out = cache[i].lds;
+            return hipSuccess;
+        }
+    hipFuncAttributes attr;
+    const hipError_t e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess) return e;
+    if (used < 128) cache[used++] = Entry{fn, attr.sharedSizeBytes};
+    *out = attr.sharedSizeBytes;
+    return hipSuccess;
+}
+
 template <typename K>
 static int launch(K kernel, const FwdArgs& a, int br, hipStream_t st, int threads, int occ) {
     const int n_qtiles = (a.Nq + br - 1) / br;
     const int64_t total = (int64_t)n_qtiles * a.B * a.H;
     size_t dyn = 0;
     if (occ > 0) {
-        hipFuncAttributes attr;
-        const hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel));
+        size_t lds = 0;
+        const hipError_t e = static_lds(reinterpret_cast<const void*>(kernel), &lds);
         if (e != hipSuccess) return (int)e;
         const size_t share = kLdsPerCu / (size_t)occ;
-        if (share > attr.sharedSizeBytes) dyn = share - attr.sharedSizeBytes;
+        if (share > lds) dyn = share - lds;
     }
     hipLaunchKernelGGL(kernel, dim3((unsigned)total), dim3(threads), dyn, st, a, n_qtiles);
     return (int)hipGetLastError();

@@ -226,29 +226,63 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                  float scale, int causal, fa_dtype dtype, void* stream);
 
-/* Static description of a status code (never NULL). */
+/*
+ * fa_status_str -- static description of a status code (never NULL). The error classes
+ * follow page "Flash Attention Shared Memory constraint", where the library reports an error
+ * instead of running when no tile configuration fits the request: FA_EUNSUPPORTED is that
+ * case here, kept apart from malformed arguments (FA_EINVAL) and runtime failures
+ * (FA_ELAUNCH).
+ */
 const char* fa_status_str(fa_status s);
 
 /*
- * fa_select_config -- the tile configuration fa_fwd would launch for these
- * sizes; pure host logic, no HIP call. Writes the query rows per workgroup
- * (*Br), the keys per K/V tile (*Bc), the waves per workgroup (*waves) and
- * the padded head dimension the kernel is compiled for (*dpad). Any output
- * pointer may be NULL. The scheduling knobs of fa_fwd_config that the built-in
- * rules set (one workgroup per CU and dispatch groups of 128 for some causal
- * fp32 problems) are not reported; they change no result bit. Returns FA_EINVAL / FA_EUNSUPPORTED like fa_fwd.
- * `num_cus` is the device's compute-unit count (256 on MI355X); it only
- * affects the query-tile height: grids of fewer 128-row workgroups than CUs
- * (than two per CU for causal grids and for fp32) take the two-way key split. Key
- * sequences of at most 512 keys (HBM-bound) use the 4-wave, 128-row kernel. The
- * answer assumes 16-byte aligned buffers; fa_fwd on unaligned buffers (or a
- * 16-bit d that is not a multiple of 8) uses the 4-wave, 128-row kernel.
+ * fa_select_config -- the tile configuration fa_fwd would launch on the current device for
+ * these sizes, without launching anything: the query rows per workgroup (*Br), the keys per
+ * K/V tile (*Bc) and the waves per workgroup (*waves). Any output pointer may be NULL.
+ *
+ * Page "Flash Attention Shared Memory constraint" searches for a tile size that fits the
+ * on-chip memory and fails with an error when none does; page "Add Fused Multi-Head
+ * Attention example" picks its tile sizes per problem. Here the choice is a function of the
+ * sizes and of the device's compute-unit count, which is read from the current HIP device
+ * (once per device, cached); with no device visible it assumes MI355X's 256. It is
+ * fa_select_config_cus with that count and the padded head dimension dropped. The answer
+ * assumes 16-byte aligned buffers; fa_fwd on unaligned buffers (or a 16-bit d that is not a
+ * multiple of 8) uses the 4-wave, 128-row kernel, and a configuration recorded by
+ * fa_tune_fwd for the same problem replaces it.
+ *
+ * Errors: FA_EINVAL / FA_EUNSUPPORTED exactly as fa_fwd for the same sizes and dtype.
  */
 fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
-                           int64_t d, int causal, int num_cus,
-                           int* Br, int* Bc, int* waves, int* dpad);
+                           int64_t d, int causal, int* Br, int* Bc, int* waves);
 
-/* Library version, for the Python binding's sanity check. */
+/*
+ * fa_select_config_cus -- the same choice as a pure function of the sizes and a given
+ * compute-unit count `num_cus` (<= 0 means 256), with no HIP call at all, so that the rules
+ * can be checked for any device on a machine without one. Also writes the padded head
+ * dimension the kernel is compiled for (*dpad, a multiple of 32). The rules:
+ *  - fp16/bf16: the two-group ping-pong kernel (256 rows, 8 waves) for aligned rows with
+ *    d % 8 == 0 and 32 < d <= 128, when its grid has at least 5/8 of a workgroup per CU
+ *    (one per CU for causal grids) and the key length passes the crossover (more than 512
+ *    keys; causal: more than 2048, or 4096 for d <= 64); otherwise the 4-wave kernel
+ *    (128 rows), or its two-way key split (64 rows, d <= 128) for grids of fewer 128-row
+ *    workgroups than CUs (than two per CU for causal grids).
+ *  - fp32: one 4-wave kernel per head dim (128 rows; 64-key tiles up to d = 96, 32-key
+ *    tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
+ *    (four per CU for causal grids).
+ * The scheduling knobs of fa_fwd_config that the built-in rules set (one workgroup per CU
+ * and dispatch groups of 128 for some causal fp32 problems) are not reported; they change
+ * no result bit.
+ */
+fa_status fa_select_config_cus(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                               int64_t d, int causal, int num_cus,
+                               int* Br, int* Bc, int* waves, int* dpad);
+
+/*
+ * fa_version -- the library's interface version (2: fa_select_config with the signature
+ * above and fa_select_config_cus). The Python binding refuses a library
+ * older than the interface it was written for. Versioning an ABI is the library's own
+ * practice; the pages prescribe none.
+ */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -29,7 +29,8 @@ def header_functions():
 def test_header_symbols_are_exported(L):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear",
-                          "fa_bwd", "fa_status_str", "fa_select_config", "fa_version"}
+                          "fa_bwd", "fa_status_str", "fa_select_config",
+                          "fa_select_config_cus", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
     assert set(fa.EXPORTED) == set(names)
@@ -298,3 +299,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         fa.lib()
+
+
+def test_select_config_current_device_matches_pure_rule(L):
+    """The section-8(b) signature reads the current device's CU count; without a visible device
+    it takes MI355X's 256, the same answer as the pure variant given 256."""
+    import torch
+    if torch.cuda.is_available():
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+    else:
+        cus = 256
+    for args in (("bf16", 4, 16, 4096, 4096, 128, False), ("f16", 2, 12, 1000, 3001, 96, False),
+                 ("f32", 1, 1, 256, 256, 64, True), ("bf16", 1, 8, 16384, 16384, 64, True)):
+        dev = fa.fa_select_config(*args, num_cus=None)
+        pure = fa.fa_select_config(*args, num_cus=cus)
+        assert dev == {k: pure[k] for k in ("Br", "Bc", "waves")}, args
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_select_config("bf16", 1, 1, 16, 16, 257, False, num_cus=None)
+    assert e.value.status == fa.FA_EUNSUPPORTED
