@@ -15,6 +15,7 @@ streams. There is no fallback: if the library is missing, the calls raise.
     attention_varlen(q, k, v, cu_q, cu_k, max_q=None, max_k=None, scale=None, causal=False)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale, causal, stream=None)
     attention_bwd(q, k, v, o, lse, do, scale=None, causal=False) -> (dq, dk, dv)
+    fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale, causal, stream=None)  # no workspace
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_ELAUNCH = 0, 1, 2, 3
 EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear", "fa_bwd",
-            "fa_status_str", "fa_select_config", "fa_select_config_cus", "fa_version")
+            "fa_bwd_noalloc", "fa_status_str", "fa_select_config", "fa_select_config_cus", "fa_version")
 ABI_VERSION = 2
 DTYPE_NAMES = {"f32": FA_F32, "f16": FA_F16, "bf16": FA_BF16}
 
@@ -86,6 +87,9 @@ def lib():
                                  ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
             L.fa_status_str.restype = ctypes.c_char_p
             L.fa_status_str.argtypes = [ctypes.c_int]
+            L.fa_bwd_noalloc.restype = ctypes.c_int
+            L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
             ip = ctypes.POINTER(ctypes.c_int)
             L.fa_select_config.restype = ctypes.c_int
             L.fa_select_config.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, ctypes.c_int, ip, ip, ip]
@@ -345,6 +349,21 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, scale: float, causal: bool, s
                           B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q), handle)
     if rc != FA_OK:
         raise FaError(rc, "fa_bwd")
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, stream=None) -> None:
+    """Calls the C-ABI fa_bwd_noalloc: fa_bwd with the library's own row-term workspace (no
+    `delta`; at most 1048576 query rows B*H*Nq; overlapping calls on one GPU race)."""
+    import torch
+    B, H, Nq, Nk, d = _check_bwd(q, k, v, o, lse, do, dq, dk, dv, None)
+    handle = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):
+        rc = lib().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  B, H, Nq, Nk, d, float(scale), int(bool(causal)), _torch_dtype_code(q),
+                                  handle)
+    if rc != FA_OK:
+        raise FaError(rc, "fa_bwd_noalloc")
 
 
 def attention_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, stream=None):

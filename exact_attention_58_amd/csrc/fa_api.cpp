@@ -239,12 +239,12 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     return launch_fwd(a, cfg, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
-// Body of fa_bwd: argument checks (before any HIP call), then the launches with `delta` as
-// the row-term workspace.
+// Shared body of fa_bwd and fa_bwd_noalloc: argument checks (before any HIP call), then the
+// launches with `delta` as the row-term workspace. check_only: stop after the checks.
 fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H,
                   int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
-                  void* stream) {
+                  void* stream, bool check_only = false) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_EINVAL;
     if (!std::isfinite(scale)) return FA_EINVAL;
     fa_status st = check_args(dtype, B, H, Nq, Nk, d);
@@ -255,6 +255,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (all % esz != 0 || (uintptr_t)lse % 4 != 0) return FA_EINVAL;
     // the backward kernels exist for the 16-bit types on 16-byte rows, d <= 128, only
     if (dtype == FA_F32 || d % 8 != 0 || d > kMaxDim32 || all % 16 != 0) return FA_EUNSUPPORTED;
+    if (check_only) return FA_OK;
     BwdArgs a;
     a.q = q;
     a.k = k;
@@ -516,6 +517,21 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     if (!delta || (uintptr_t)delta % 4 != 0) return FA_EINVAL;
     return fa::run_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, d, scale, causal, dtype,
                        stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, fa_dtype dtype,
+                         void* stream) {
+    // the same checks as fa_bwd first, so that every error path stays free of HIP calls
+    fa_status st = fa::run_bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, H, Nq, Nk, d, scale,
+                               causal, dtype, stream, /*check_only=*/true);
+    if (st != FA_OK) return st;
+    // the row terms (one fp32 per query row) must fit the library's own workspace
+    if (B * H * Nq > fa::kBwdScratchFloats) return FA_EUNSUPPORTED;
+    float* ws = nullptr;
+    if (fa::bwd_scratch(&ws) != 0 || ws == nullptr) return FA_ELAUNCH;
+    return fa::run_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, Nq, Nk, d, scale, causal, dtype, stream);
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -408,7 +410,32 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices];  // per device, resolved on first use
+
 }  // namespace
+
+// Row-term workspace of the allocation-free backward entry point. In host code this name is a
+// host-side stand-in: kernels receive the device address hipGetSymbolAddress reports for the
+// current device, never the name itself.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+int bwd_scratch(float** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        g_scratch_ptr[dev] = (float*)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return (int)hipSuccess;
+}
 
 int launch_bwd(const BwdArgs& a, int dpad, void* stream) {
     hipStream_t st = (hipStream_t)stream;

@@ -70,4 +70,12 @@ struct BwdArgs {
 // hipError_t of the launches as int.
 int launch_bwd(const BwdArgs& a, int dpad, void* stream);
 
+// The backward's own row-term workspace for callers that cannot allocate: a file-scope device
+// array of kBwdScratchFloats fp32 values (4 MiB, one value per query row) that every GPU the
+// library runs on holds until the process ends. bwd_scratch() gives its address on the current
+// device (resolved once per device); returns the hipError_t as int. Calls that overlap on one
+// GPU share the array and race.
+constexpr int64_t kBwdScratchFloats = (int64_t)1 << 20;
+int bwd_scratch(float** out);
+
 }  // namespace fa

@@ -227,6 +227,27 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  float scale, int causal, fa_dtype dtype, void* stream);
 
 /*
+ * fa_bwd_noalloc -- fa_bwd without the caller's workspace, for callers that cannot allocate
+ * device memory or pass one (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).
+ *
+ * Same arguments, results and errors as fa_bwd minus `delta`: the row terms live in a
+ * file-scope device array of the library (4 MiB, one fp32 per query row) that each GPU the
+ * library runs on holds until the process ends; its address is looked up once per device on
+ * the first call there. The call itself allocates nothing.
+ *
+ * Limit: B * H * Nq <= 1048576 query rows; larger requests return FA_EUNSUPPORTED before any
+ * HIP call. The array is overwritten in full by every call before it is read, so nothing has
+ * to be cleared, but all calls on one GPU share it: calls that overlap on one GPU (two
+ * streams, two threads) race and give undefined gradients. FA_ELAUNCH also when the array's
+ * device address cannot be obtained.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                         float scale, int causal, fa_dtype dtype, void* stream);
+
+/*
  * fa_status_str -- static description of a status code (never NULL). The error classes
  * follow page "Flash Attention Shared Memory constraint", where the library reports an error
  * instead of running when no tile configuration fits the request: FA_EUNSUPPORTED is that
@@ -279,7 +300,7 @@ fa_status fa_select_config_cus(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq,
 
 /*
  * fa_version -- the library's interface version (2: fa_select_config with the signature
- * above and fa_select_config_cus). The Python binding refuses a library
+ * above, fa_select_config_cus and fa_bwd_noalloc). The Python binding refuses a library
  * older than the interface it was written for. Versioning an ABI is the library's own
  * practice; the pages prescribe none.
  */

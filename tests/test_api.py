@@ -29,7 +29,7 @@ def header_functions():
 def test_header_symbols_are_exported(L):
     names = header_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_varlen", "fa_fwd_config", "fa_tune_fwd", "fa_tune_clear",
-                          "fa_bwd", "fa_status_str", "fa_select_config",
+                          "fa_bwd", "fa_bwd_noalloc", "fa_status_str", "fa_select_config",
                           "fa_select_config_cus", "fa_version"}
     for n in names:
         assert hasattr(L, n), n
