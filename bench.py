@@ -409,7 +409,7 @@ def main():
                 f"{ow.dtype} peak; median {st['median_ms']} ms over {st['launches']} launches")
         # backward (FLOP convention: 2.5 x the forward's, i.e. five products of the forward's
         # size; this implementation recomputes S and dP in both tile kernels)
-        for name in ("d128_bf16", "d128_bf16_causal", "long_causal_bf16"):
+        for name in ("d128_bf16", "d128_bf16_causal", "long_causal_bf16", "pages_f32"):
             ow = WORKLOADS[name]
             ms = time_backward(fa, torch, ow, max(5, min(args.steps, 20)), 2)
             tf = 2.5 * ow.flops / (ms * 1e-3) / 1e12

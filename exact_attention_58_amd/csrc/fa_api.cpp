@@ -253,8 +253,9 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
                           (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv;
     const int esz = dtype == FA_F32 ? 4 : 2;
     if (all % esz != 0 || (uintptr_t)lse % 4 != 0) return FA_EINVAL;
-    // the backward kernels exist for the 16-bit types on 16-byte rows, d <= 128, only
-    if (dtype == FA_F32 || d % 8 != 0 || d > kMaxDim32 || all % 16 != 0) return FA_EUNSUPPORTED;
+    // the backward kernels exist for head dims up to 128, every dtype
+    if (d > kMaxDim32) return FA_EUNSUPPORTED;
+    const bool vec = all % 16 == 0 && (d * esz) % 16 == 0;
     if (check_only) return FA_OK;
     BwdArgs a;
     a.q = q;
@@ -277,7 +278,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     a.causal = causal ? 1 : 0;
     a.dtype = (int)dtype;
     const int dpad = (int)((d + 31) / 32) * 32;
-    return launch_bwd(a, dpad, stream) == 0 ? FA_OK : FA_ELAUNCH;
+    return launch_bwd(a, dpad, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }
 
 }  // namespace

@@ -24,6 +24,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -60,9 +61,37 @@ void bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, float* delta, int
     if (r < rows && sub == 0) delta[r] = acc;
 }
 
+// One element of a row-major buffer of type E (fp32, or a 16-bit type), as fp32 (exact).
+template <typename E>
+__device__ inline float elem(const void* p, int64_t i) {
+    if constexpr (std::is_same<E, float>::value) {
+        return ((const float*)p)[i];
+    } else if constexpr (std::is_same<E, __bf16>::value) {
+        return __uint_as_float((unsigned)((const uint16_t*)p)[i] << 16);
+    } else {
+        return (float)((const _Float16*)p)[i];
+    }
+}
+
+// Row terms for any element type, head dim and alignment: sixteen lanes share a row and walk
+// its elements sixteen apart (each load instruction reads 16 consecutive elements of four
+// rows), then meet through lane shuffles.
+template <typename E>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void bwd_delta_any_kernel(const void* o, const void* dout, float* delta, int64_t rows, int d) {
+    const int sub = threadIdx.x & 15;
+    const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    float acc = 0.0f;
+    if (r < rows)
+        for (int c = sub; c < d; c += 16) acc = __builtin_fmaf(elem<E>(o, r * d + c), elem<E>(dout, r * d + c), acc);
+#pragma unroll
+    for (int m = 8; m >= 1; m /= 2) acc += __shfl_xor(acc, m, 16);
+    if (r < rows && sub == 0) delta[r] = acc;
+}
+
 // Tile of 64 rows x DP columns (16-bit) staged through registers into LDS rows of STR
-// elements; rows >= nrows and columns >= d are zero.
-template <int DP, int STR>
+// elements; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0, aligned).
+template <int DP, int STR, bool VEC>
 struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
     static constexpr int CH = 64 * CPR / 256;         // chunks per thread
@@ -73,7 +102,7 @@ struct TileCopy {
         for (int c = 0; c < CH; ++c) {
             const int chunk = tid + c * 256;
             const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            r[c] = load_chunk16<true>(base, row0 + row, col, nrows, d);
+            r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
         }
     }
     __device__ __attribute__((always_inline)) void store(uint16_t* lds, int tid) const {
@@ -105,7 +134,7 @@ __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* t
 // share a SIMD whenever the registers fit (up to d = 96 for MODE 0, every d for the single
 // modes): one wave's LDS reads and staged loads then overlap the other's products, about
 // 1.5x the throughput of one wave per SIMD.
-template <typename T, int DP, bool CAUSAL, int MODE>
+template <typename T, int DP, bool CAUSAL, int MODE, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DP <= 96 || MODE != 0 ? 2 : 1, DP <= 96 || MODE != 0 ? 2 : 1)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
@@ -139,8 +168,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     u32x4 kf[NDS], vf[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-        kf[ds] = load_chunk16<true>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
-        if constexpr (DO_DK) vf[ds] = load_chunk16<true>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
+        kf[ds] = load_chunk16<VEC>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
+        if constexpr (DO_DK) vf[ds] = load_chunk16<VEC>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
     }
 
     f32x16 dva[NDB], dka[NDB];
@@ -151,7 +180,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     // query tiles that see any key of this workgroup (causal: queries >= k0)
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
-    TileCopy<DP, STR> qc, gc;
+    TileCopy<DP, STR, VEC> qc, gc;
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int qt) __attribute__((always_inline)) {
         qc.load(qg, qt * BQ, Nq, d, tid);
@@ -259,7 +288,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 // ---------------------------------------------------------------- dQ
 
 // Two waves per SIMD at every head dim (the registers fit 256 per wave).
-template <typename T, int DP, bool CAUSAL>
+template <typename T, int DP, bool CAUSAL, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     constexpr int BR = 128, BC = 64;  // queries per workgroup, keys per tile
@@ -288,8 +317,8 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     u32x4 qf[NDS], gf[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-        qf[ds] = load_chunk16<true>(qg, myq, ds * 16 + 8 * h32, Nq, d);
-        gf[ds] = load_chunk16<true>(gg, myq, ds * 16 + 8 * h32, Nq, d);
+        qf[ds] = load_chunk16<VEC>(qg, myq, ds * 16 + 8 * h32, Nq, d);
+        gf[ds] = load_chunk16<VEC>(gg, myq, ds * 16 + 8 * h32, Nq, d);
     }
     const float lq = myq < Nq ? a.lse[(int64_t)bh * Nq + myq] * kLog2e : 0.0f;
     const float dq = myq < Nq ? a.delta[(int64_t)bh * Nq + myq] : 0.0f;
@@ -303,7 +332,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
-    TileCopy<DP, STR> kc, vc;
+    TileCopy<DP, STR, VEC> kc, vc;
     kc.load(kg, 0, Nk, d, tid);
     vc.load(vg, 0, Nk, d, tid);
     for (int j = 0; j < n_tiles; ++j) {
@@ -364,39 +393,341 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d0 = db * 32 + 8 * g + 4 * h32;
-                if (d0 < d) {
-                    u32x2 w = {Half<T>::pack2(dqa[db][4 * g + 0] * sc, dqa[db][4 * g + 1] * sc),
-                               Half<T>::pack2(dqa[db][4 * g + 2] * sc, dqa[db][4 * g + 3] * sc)};
-                    *(u32x2*)(og + d0) = w;
+                if (VEC) {
+                    if (d0 < d) {
+                        u32x2 w = {Half<T>::pack2(dqa[db][4 * g + 0] * sc, dqa[db][4 * g + 1] * sc),
+                                   Half<T>::pack2(dqa[db][4 * g + 2] * sc, dqa[db][4 * g + 3] * sc)};
+                        *(u32x2*)(og + d0) = w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < d) og[d0 + e] = Half<T>::one(dqa[db][4 * g + e] * sc);
                 }
             }
     }
 }
 
-template <typename T, int DP>
-int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+// ---------------------------------------------------------------- fp32
+
+// Tile of ROWS rows x DP columns (fp32) staged through registers into LDS rows of STR floats;
+// rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 4 == 0, aligned buffers).
+template <int ROWS, int DP, int STR, bool VEC>
+struct TileCopy32 {
+    static constexpr int CPR = DP / 4;                  // 16-byte chunks per row
+    static constexpr int CH = ROWS * CPR / 256;         // chunks per thread
+    static_assert(ROWS * CPR % 256 == 0, "tile split");
+    f32x4 r[CH];
+    __device__ __attribute__((always_inline)) void load(const float* base, int row0, int nrows, int d, int tid) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int chunk = tid + c * 256;
+            const int row = chunk / CPR, col = (chunk % CPR) * 4;
+            r[c] = load_chunk32<VEC>(base, row0 + row, col, nrows, d);
+        }
+    }
+    __device__ __attribute__((always_inline)) void store(float* lds, int tid) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int chunk = tid + c * 256;
+            const int row = chunk / CPR, col = (chunk % CPR) * 4;
+            *(f32x4*)(lds + row * STR + col) = r[c];
+        }
+    }
+};
+
+// Half a row of fp32 (HALF = DP/2 values from column h32*HALF) into registers: the B operand
+// of a 32x32x2 fp32 product whose reduction over the head dim runs as d = h32*HALF + i.
+template <int HALF, bool VEC>
+__device__ __attribute__((always_inline)) inline void load_half_row(float (&dst)[HALF], const float* base, int row,
+                                                                    int nrows, int d, int h32) {
+#pragma unroll
+    for (int c4 = 0; c4 < HALF / 4; ++c4) {
+        const f32x4 t = load_chunk32<VEC>(base, row, h32 * HALF + 4 * c4, nrows, d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[4 * c4 + e] = t[e];
+    }
+}
+
+// fp32 dK, dV on v_mfma_f32_32x32x2_f32, the layout of the fp32 forward mirrored: one
+// workgroup per 128 keys (4 waves x 32 keys), looping over query tiles of 32. S = Q K^T and
+// dP = dO V^T take this wave's keys as the MFMA columns (K and V half rows in registers, Q and
+// dO read from LDS along the head dim), so a lane holds one key and 16 queries; register r of
+// S is then, with the queries of the reduction enumerated in accumulator order, the A operand
+// of dV += P^T dO (and dS of dK += dS^T Q), whose B operand is one dO (Q) row element per lane
+// read from LDS. MODE as in the 16-bit kernel (0: dK and dV, 1: dV only, 2: dK only).
+template <int DP, bool CAUSAL, int MODE, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
+                          amdgpu_waves_per_eu(DP <= 64 || MODE == 1 ? 2 : 1, DP <= 64 || MODE == 1 ? 2 : 1)))
+void bwd32_dkdv_kernel(BwdArgs a, int n_ktiles) {
+    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
+    constexpr int BK = 128, BQ = 32;  // keys per workgroup, queries per tile
+    constexpr int STR = DP + 4;       // LDS row stride (floats): 16-byte pad
+    constexpr int HALF = DP / 2, NDB = DP / 32;
+    __shared__ __attribute__((aligned(16))) float Qs[BQ * STR];
+    __shared__ __attribute__((aligned(16))) float Gs[BQ * STR];  // dO
+    __shared__ __attribute__((aligned(16))) float Ls[BQ];
+    __shared__ __attribute__((aligned(16))) float Ds[BQ];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, kXcdSlots);
+    const int bh = pt.pair, kt = pt.tile;
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * wave;
+    const int mykey = kw0 + l32;
+
+    const float* qg = (const float*)a.q + (int64_t)bh * Nq * d;
+    const float* kg = (const float*)a.k + (int64_t)bh * Nk * d;
+    const float* vg = (const float*)a.v + (int64_t)bh * Nk * d;
+    const float* gg = (const float*)a.dout + (int64_t)bh * Nq * d;
+    const float* lg = a.lse + (int64_t)bh * Nq;
+    const float* dg = a.delta + (int64_t)bh * Nq;
+
+    // this wave's keys as B operands: lane holds K[mykey][h32*HALF + i] (V likewise)
+    float kf[HALF], vf[HALF];
+    load_half_row<HALF, VEC>(kf, kg, mykey, Nk, d, h32);
+    if constexpr (DO_DK) load_half_row<HALF, VEC>(vf, vg, mykey, Nk, d, h32);
+
+    f32x16 dva[NDB], dka[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dva[i] = dka[i] = f32x16{};
+    const float c = a.scale_log2;
+
+    // query tiles that see any key of this workgroup (causal: queries >= k0)
+    const int qt0 = CAUSAL ? k0 / BQ : 0;
+    const int n_qt = (Nq + BQ - 1) / BQ;
+    TileCopy32<BQ, DP, STR, VEC> qc, gc;
+    float lrow = 0.0f, drow = 0.0f;
+    auto load_tile = [&](int qt) __attribute__((always_inline)) {
+        qc.load(qg, qt * BQ, Nq, d, tid);
+        gc.load(gg, qt * BQ, Nq, d, tid);
+        if (tid < BQ) {
+            const int q = qt * BQ + tid;
+            lrow = q < Nq ? lg[q] * kLog2e : 0.0f;
+            drow = q < Nq ? dg[q] : 0.0f;
+        }
+    };
+    if (qt0 < n_qt) load_tile(qt0);
+    for (int qt = qt0; qt < n_qt; ++qt) {
+        __syncthreads();
+        qc.store(Qs, tid);
+        gc.store(Gs, tid);
+        if (tid < BQ) {
+            Ls[tid] = lrow;
+            Ds[tid] = drow;
+        }
+        __syncthreads();
+        if (qt + 1 < n_qt) load_tile(qt + 1);
+        const int q0 = qt * BQ;
+        // a causal wave skips tiles whose queries all precede its keys
+        if (CAUSAL && q0 + BQ - 1 < kw0) continue;
+
+        // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys; register r holds query
+        // q0 + 8 (r/4) + 4 h32 + r%4 and key mykey
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const float* qp = Qs + l32 * STR + h32 * HALF;
+        const float* gp = Gs + l32 * STR + h32 * HALF;
+#pragma unroll
+        for (int c4 = 0; c4 < HALF / 4; ++c4) {
+            const f32x4 qa = *(const f32x4*)(qp + 4 * c4);
+            f32x4 ga = {};
+            if constexpr (DO_DK) ga = *(const f32x4*)(gp + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[e], kf[4 * c4 + e], s, 0, 0, 0);
+                if constexpr (DO_DK) dp = __builtin_amdgcn_mfma_f32_32x32x2f32(ga[e], vf[4 * c4 + e], dp, 0, 0, 0);
+            }
+        }
+        // the weight is kept iff off = 8 (r/4) + r%4 >= lo (the causal diagonal and the key
+        // tail in one compare); padded query rows have zero Q, dO, L and D and add nothing
+        const int lo = mykey >= Nk ? 64 : CAUSAL ? mykey - q0 - 4 * h32 : -64;
+        float pr[16], dsr[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int ql = 8 * g + 4 * h32;
+            const f32x4 lv = *(const f32x4*)(Ls + ql);
+            f32x4 dv = {};
+            if constexpr (DO_DK) dv = *(const f32x4*)(Ds + ql);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
+                pr[4 * g + e] = p;
+                if constexpr (DO_DK) dsr[4 * g + e] = p * (dp[4 * g + e] - dv[e]);
+            }
+        }
+        // dV += P^T dO and dK += dS^T Q: k-step r reduces over the two queries lane halves hold
+        // in register r; the B operand is that query's row, one element per lane
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * h32 + (r & 3);
+            const float* grow = Gs + row * STR + l32;
+            const float* qrow = Qs + row * STR + l32;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                if constexpr (DO_DV) dva[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(pr[r], grow[db * 32], dva[db], 0, 0, 0);
+                if constexpr (DO_DK) dka[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(dsr[r], qrow[db * 32], dka[db], 0, 0, 0);
+            }
+        }
+    }
+
+    // register r of block db: key kw0 + 8 (r/4) + 4 h32 + r%4, column db*32 + l32
+    float* dkg = (float*)a.dk + (int64_t)bh * Nk * d;
+    float* dvg = (float*)a.dv + (int64_t)bh * Nk * d;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        const int col = db * 32 + l32;
+        if (col >= d) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+            if (key < Nk) {
+                if constexpr (DO_DV) dvg[(int64_t)key * d + col] = dva[db][r];
+                if constexpr (DO_DK) dkg[(int64_t)key * d + col] = dka[db][r] * sc;
+            }
+        }
+    }
+}
+
+// fp32 dQ on v_mfma_f32_32x32x2_f32: one workgroup per 128 queries (4 waves x 32), looping over
+// key tiles of 32, in the fp32 forward's layout: S^T = K Q^T and dP^T = V dO^T with this wave's
+// queries as the columns (Q and dO half rows in registers, K and V from LDS along the head
+// dim), so dS^T register r is the B operand of dQ^T += K^T dS^T, whose A operand is one K row
+// element per lane read from LDS.
+template <int DP, bool CAUSAL, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(DP <= 64 ? 2 : 1, DP <= 64 ? 2 : 1)))
+void bwd32_dq_kernel(BwdArgs a, int n_qtiles) {
+    constexpr int BR = 128, BC = 32;  // queries per workgroup, keys per tile
+    constexpr int STR = DP + 4;
+    constexpr int HALF = DP / 2, NDB = DP / 32;
+    __shared__ __attribute__((aligned(16))) float Ks[BC * STR];
+    __shared__ __attribute__((aligned(16))) float Vs[BC * STR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL, kXcdSlots);
+    const int bh = pt.pair;
+    int qt = pt.tile;
+    if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int q0 = qt * BR;
+    const int r0w = q0 + 32 * wave;
+    const int myq = r0w + l32;
+
+    const float* qg = (const float*)a.q + (int64_t)bh * Nq * d;
+    const float* kg = (const float*)a.k + (int64_t)bh * Nk * d;
+    const float* vg = (const float*)a.v + (int64_t)bh * Nk * d;
+    const float* gg = (const float*)a.dout + (int64_t)bh * Nq * d;
+
+    float qf[HALF], gf[HALF];
+    load_half_row<HALF, VEC>(qf, qg, myq, Nq, d, h32);
+    load_half_row<HALF, VEC>(gf, gg, myq, Nq, d, h32);
+    const float lq = myq < Nq ? a.lse[(int64_t)bh * Nq + myq] * kLog2e : 0.0f;
+    const float dq = myq < Nq ? a.delta[(int64_t)bh * Nq + myq] : 0.0f;
+    const float c = a.scale_log2;
+
+    int kv_end = Nk;
+    if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
+    const int n_tiles = (kv_end + BC - 1) / BC;
+
+    f32x16 dqa[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
+
+    TileCopy32<BC, DP, STR, VEC> kc, vc;
+    kc.load(kg, 0, Nk, d, tid);
+    vc.load(vg, 0, Nk, d, tid);
+    for (int j = 0; j < n_tiles; ++j) {
+        __syncthreads();
+        kc.store(Ks, tid);
+        vc.store(Vs, tid);
+        __syncthreads();
+        if (j + 1 < n_tiles) {
+            kc.load(kg, (j + 1) * BC, Nk, d, tid);
+            vc.load(vg, (j + 1) * BC, Nk, d, tid);
+        }
+        const int k0 = j * BC;
+        if (CAUSAL && k0 > r0w + 31) continue;
+
+        // S^T = K Q^T and dP^T = V dO^T: register r is key k0 + 8 (r/4) + 4 h32 + r%4, query myq
+        f32x16 s = f32x16{}, dp = f32x16{};
+        const float* kp = Ks + l32 * STR + h32 * HALF;
+        const float* vp = Vs + l32 * STR + h32 * HALF;
+#pragma unroll
+        for (int c4 = 0; c4 < HALF / 4; ++c4) {
+            const f32x4 ka = *(const f32x4*)(kp + 4 * c4);
+            const f32x4 va = *(const f32x4*)(vp + 4 * c4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[e], qf[4 * c4 + e], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x2f32(va[e], gf[4 * c4 + e], dp, 0, 0, 0);
+            }
+        }
+        const int lim = (CAUSAL ? min(Nk - 1, myq) : Nk - 1) - k0 - 4 * h32;
+        float dsr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            const float p = off <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq)) : 0.0f;
+            dsr[r] = p * (dp[r] - dq);
+        }
+        // dQ^T += K^T dS^T: k-step r reduces over the two keys lane halves hold in register r
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float* krow = Ks + (8 * (r >> 2) + 4 * h32 + (r & 3)) * STR + l32;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                dqa[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(krow[db * 32], dsr[r], dqa[db], 0, 0, 0);
+        }
+    }
+
+    // register r of block db: column db*32 + 8 (r/4) + 4 h32 + r%4, query myq
+    if (myq < Nq) {
+        float* og = (float*)a.dq + ((int64_t)bh * Nq + myq) * d;
+        const float sc = a.scale;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * h32;
+                const f32x4 w = {dqa[db][4 * g + 0] * sc, dqa[db][4 * g + 1] * sc, dqa[db][4 * g + 2] * sc,
+                                 dqa[db][4 * g + 3] * sc};
+                if (VEC) {
+                    if (d0 < d) *(f32x4*)(og + d0) = w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < d) og[d0 + e] = w[e];
+                }
+            }
+    }
+}
+
+template <int DP, bool VEC>
+int launch_bwd32(const BwdArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.H * a.Nq;
-    static_assert(DP <= 128, "row terms: at most 16 chunks of 8 per row");
     if ((rows + 15) / 16 > INT32_MAX) return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, a.d);
+    hipLaunchKernelGGL(bwd_delta_any_kernel<float>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
+                       a.o, a.dout, a.delta, rows, a.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
     const int n_kt = (a.Nk + 127) / 128;
     const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
-    if constexpr (DP <= 96) {
+    if constexpr (DP <= 64) {
         if (a.causal)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 0>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, true, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
         else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 0>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, false, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
     } else {
-        // dV and dK as two kernels that each fit two waves per SIMD
+        // dV and dK as two kernels, each holding half the accumulators
         if (a.causal) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 1>), dim3(g1), dim3(256), 0, st, a, n_kt);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 2>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, true, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, true, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
         } else {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 1>), dim3(g1), dim3(256), 0, st, a, n_kt);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 2>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, false, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd32_dkdv_kernel<DP, false, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
         }
     }
     e = hipGetLastError();
@@ -404,10 +735,73 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int n_qt = (a.Nq + 127) / 128;
     const unsigned g2 = (unsigned)((int64_t)n_qt * a.B * a.H);
     if (a.causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, true>), dim3(g2), dim3(256), 0, st, a, n_qt);
+        hipLaunchKernelGGL((bwd32_dq_kernel<DP, true, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, false>), dim3(g2), dim3(256), 0, st, a, n_qt);
+        hipLaunchKernelGGL((bwd32_dq_kernel<DP, false, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
     return (int)hipGetLastError();
+}
+
+template <typename T, int DP, bool VEC>
+int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.H * a.Nq;
+    static_assert(DP <= 128, "row terms: at most 16 chunks of 8 per row");
+    if ((rows + 15) / 16 > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+    if (VEC)
+        hipLaunchKernelGGL(bwd_delta_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
+                           (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, a.d);
+    else
+        hipLaunchKernelGGL(bwd_delta_any_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st,
+                           a.o, a.dout, a.delta, rows, a.d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int n_kt = (a.Nk + 127) / 128;
+    const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
+    if constexpr (DP <= 96) {
+        if (a.causal)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+    } else {
+        // dV and dK as two kernels that each fit two waves per SIMD
+        if (a.causal) {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        } else {
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        }
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+    const int n_qt = (a.Nq + 127) / 128;
+    const unsigned g2 = (unsigned)((int64_t)n_qt * a.B * a.H);
+    if (a.causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, true, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, false, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
+    return (int)hipGetLastError();
+}
+
+template <typename T, bool VEC>
+int launch_bwd_16(const BwdArgs& a, int dpad, hipStream_t st) {
+    switch (dpad) {
+        case 32: return launch_bwd_t<T, 32, VEC>(a, st);
+        case 64: return launch_bwd_t<T, 64, VEC>(a, st);
+        case 96: return launch_bwd_t<T, 96, VEC>(a, st);
+        case 128: return launch_bwd_t<T, 128, VEC>(a, st);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+template <bool VEC>
+int launch_bwd_32(const BwdArgs& a, int dpad, hipStream_t st) {
+    switch (dpad) {
+        case 32: return launch_bwd32<32, VEC>(a, st);
+        case 64: return launch_bwd32<64, VEC>(a, st);
+        case 96: return launch_bwd32<96, VEC>(a, st);
+        case 128: return launch_bwd32<128, VEC>(a, st);
+        default: return (int)hipErrorInvalidValue;
+    }
 }
 
 constexpr int kMaxScratchDevices = 64;
@@ -437,16 +831,11 @@ int bwd_scratch(float** out) {
     return (int)hipSuccess;
 }
 
-int launch_bwd(const BwdArgs& a, int dpad, void* stream) {
+int launch_bwd(const BwdArgs& a, int dpad, bool vec, void* stream) {
     hipStream_t st = (hipStream_t)stream;
-    const bool bf = a.dtype == 2;
-    switch (dpad) {
-        case 32: return bf ? launch_bwd_t<__bf16, 32>(a, st) : launch_bwd_t<_Float16, 32>(a, st);
-        case 64: return bf ? launch_bwd_t<__bf16, 64>(a, st) : launch_bwd_t<_Float16, 64>(a, st);
-        case 96: return bf ? launch_bwd_t<__bf16, 96>(a, st) : launch_bwd_t<_Float16, 96>(a, st);
-        case 128: return bf ? launch_bwd_t<__bf16, 128>(a, st) : launch_bwd_t<_Float16, 128>(a, st);
-        default: return (int)hipErrorInvalidValue;
-    }
+    if (a.dtype == 0) return vec ? launch_bwd_32<true>(a, dpad, st) : launch_bwd_32<false>(a, dpad, st);
+    if (a.dtype == 2) return vec ? launch_bwd_16<__bf16, true>(a, dpad, st) : launch_bwd_16<__bf16, false>(a, dpad, st);
+    return vec ? launch_bwd_16<_Float16, true>(a, dpad, st) : launch_bwd_16<_Float16, false>(a, dpad, st);
 }
 
 }  // namespace fa

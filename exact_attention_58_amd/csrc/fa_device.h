@@ -179,4 +179,20 @@ __device__ inline u32x4 load_chunk16(const uint16_t* base, int row, int col, int
     return r;
 }
 
+// One 16-byte chunk (4 floats) of row `row`, columns [col, col+4), zero outside
+// [0, nrows) x [0, ncols). VEC: rows are 16-byte aligned and ncols % 4 == 0.
+template <bool VEC>
+__device__ inline f32x4 load_chunk32(const float* base, int row, int col, int nrows, int ncols) {
+    f32x4 r = {0.f, 0.f, 0.f, 0.f};
+    if (row >= nrows) return r;
+    const float* p = base + (int64_t)row * ncols + col;
+    if (VEC) {
+        if (col < ncols) r = *(const f32x4*)p;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = (col + i < ncols) ? p[i] : 0.0f;
+    }
+    return r;
+}
+
 }  // namespace fa

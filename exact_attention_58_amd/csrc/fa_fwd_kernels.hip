@@ -742,21 +742,6 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
 
 // ---------------------------------------------------------------- fp32
 
-// One 16-byte chunk (4 floats) of row `row`, columns [col, col+4), zero outside.
-template <bool VEC>
-__device__ inline f32x4 load_chunk32(const float* base, int row, int col, int nrows, int ncols) {
-    f32x4 r = {0.f, 0.f, 0.f, 0.f};
-    if (row >= nrows) return r;
-    const float* p = base + (int64_t)row * ncols + col;
-    if (VEC) {
-        if (col < ncols) r = *(const f32x4*)p;
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = (col + i < ncols) ? p[i] : 0.0f;
-    }
-    return r;
-}
-
 // fp32 forward kernel on v_mfma_f32_32x32x2_f32. The head-dim reduction of S^T is
 // enumerated as d = h32*(DP/2) + ds so each lane loads half a contiguous row of Q
 // and of K. P stays fp32 for the PV product. SPLIT = 2 (grids too small to fill the chip)

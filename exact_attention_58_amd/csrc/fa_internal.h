@@ -46,8 +46,7 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
 // Launches the kernel for `cfg` on `stream`; returns the hipError_t of the launch as int.
 int launch_fwd(const FwdArgs& a, const TileConfig& cfg, bool vec, void* stream);
 
-// Everything the backward kernels need, already validated by the front end (16-bit types,
-// d % 8 == 0, 16-byte aligned buffers).
+// Everything the backward kernels need, already validated by the front end (d <= 128).
 struct BwdArgs {
     const void* q;
     const void* k;
@@ -66,9 +65,9 @@ struct BwdArgs {
     int dtype;
 };
 
-// Launches the three backward kernels (row terms, dK/dV, dQ) on `stream`; returns the
-// hipError_t of the launches as int.
-int launch_bwd(const BwdArgs& a, int dpad, void* stream);
+// Launches the backward kernels (row terms, dK/dV, dQ) on `stream`; `vec`: every buffer
+// 16-byte aligned and d * element size a multiple of 16. Returns the hipError_t as int.
+int launch_bwd(const BwdArgs& a, int dpad, bool vec, void* stream);
 
 // The backward's own row-term workspace for callers that cannot allocate: a file-scope device
 // array of kBwdScratchFloats fp32 values (4 MiB, one value per query row) that every GPU the

@@ -217,9 +217,13 @@ void fa_tune_clear(void);
  * including the workspace; the library allocates nothing. dq, dk, dv and delta must not
  * alias each other or any input.
  *
- * Errors: as fa_fwd (checked before any HIP call). FA_EUNSUPPORTED also for fp32 inputs,
- * for d not a multiple of 8 and for 16-bit buffers that are not 16-byte aligned: the
- * backward kernels exist for bf16/fp16 rows of whole 16-byte chunks only.
+ * Every dtype of fa_fwd is served, with 1 <= d <= 128: fp32 inputs on fp32 MFMA with P and dS
+ * kept in fp32; fp16/bf16 inputs with P and dS rounded to the input type for the products that
+ * consume them. Buffers need only their element's alignment; 16-byte aligned buffers with
+ * d * element size a multiple of 16 take vectorised loads.
+ *
+ * Errors: as fa_fwd (checked before any HIP call), plus FA_EINVAL for a null or misaligned
+ * delta, and FA_EUNSUPPORTED for d > 128.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                  const void* dout, void* dq, void* dk, void* dv, float* delta,

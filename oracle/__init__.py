@@ -101,7 +101,7 @@ def attention_fwd(q, k, v, scale: float, causal: bool, rows=None, threads: int |
     return o, lse
 
 
-def attention_bwd(q, k, v, do, scale: float, causal: bool):
+def attention_bwd(q, k, v, do, scale: float, causal: bool, o=None):
     """Exact gradients of the attention forward in fp64 (numpy, whole score matrix per head).
 
     For O = softmax(S) V with S = scale * Q K^T (top-left causal mask: key j visible to query
@@ -119,6 +119,11 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
     matrices with no tiling, no recomputation from L and no online recurrence. rowsum(P dP)
     equals rowsum(dO * O) exactly in real arithmetic.
 
+    o: None, or the forward output as the caller stored it ([B,H,Nq,d]). That page's backward
+    kernel forms its row term from the stored output, D_i = rowsum(dO_i * O_i); given o, the
+    row term is that sum over o (equal to rowsum(P dP) when o is the exact output). A stored
+    output rounded to 16 bits then enters D exactly as it enters the kernels.
+
     q: [B,H,Nq,d], k, v: [B,H,Nk,d], do: [B,H,Nq,d]. Returns dq, dk, dv (fp64).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -128,6 +133,10 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
     if q.ndim != 4 or k.shape[:2] != q.shape[:2] or v.shape != k.shape or do.shape != q.shape \
             or k.shape[3] != q.shape[3]:
         raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape} do{do.shape}")
+    if o is not None:
+        o = np.asarray(o, dtype=np.float64)
+        if o.shape != q.shape:
+            raise ValueError(f"o must be shaped like q: {o.shape} vs {q.shape}")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     dq = np.empty_like(q)
@@ -145,7 +154,11 @@ def attention_bwd(q, k, v, do, scale: float, causal: bool):
             p = e / e.sum(axis=1, keepdims=True)
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
-            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            if o is None:
+                D = (p * dp).sum(axis=1, keepdims=True)
+            else:
+                D = (do[b, h] * o[b, h]).sum(axis=1, keepdims=True)
+            ds = p * (dp - D)
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv

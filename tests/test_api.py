@@ -155,16 +155,15 @@ def call_bwd(L, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, delta=P, B=1,
     dict(B=0), dict(Nq=0), dict(Nk=0), dict(d=0), dict(dtype=3),
     dict(scale=float("nan")), dict(B=2**40, H=2**40),
     dict(do=P + 1), dict(dv=P + 1), dict(lse=P + 2), dict(delta=P + 2),
+    dict(q=P + 2, dtype=0), dict(dk=P + 2, dtype=0),   # fp32 buffers need 4-byte alignment
 ])
 def test_bwd_invalid_arguments(L, kw):
     assert call_bwd(L, **kw) == fa.FA_EINVAL
 
 
-@pytest.mark.parametrize("kw", [
-    dict(d=136), dict(d=256), dict(dtype=0), dict(d=60), dict(d=5), dict(q=P + 2), dict(dk=P + 8),
-])
+@pytest.mark.parametrize("kw", [dict(d=136), dict(d=256), dict(d=129, dtype=0), dict(d=200, dtype=1)])
 def test_bwd_unsupported(L, kw):
-    """fp32, d not a multiple of 8 and 16-bit rows off 16-byte alignment have no backward kernel."""
+    """Head dims past 128 have no backward kernel (every dtype)."""
     assert call_bwd(L, **kw) == fa.FA_EUNSUPPORTED
 
 

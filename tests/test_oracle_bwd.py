@@ -149,3 +149,44 @@ def test_bad_shapes_raise():
         oracle.attention_bwd(q, rand((1, 1, 4, 3), 2), rand((1, 1, 4, 3), 3), q, 1.0, False)
     with pytest.raises(ValueError):
         oracle.attention_bwd(q, rand((1, 1, 4, 2), 2), rand((1, 1, 4, 2), 3), rand((1, 1, 4, 2), 4), 1.0, False)
+
+
+def _probs(q, k, scale, causal):
+    """Softmax weights written out separately (numpy, per head)."""
+    s = scale * np.einsum("bhqd,bhkd->bhqk", q, k)
+    if causal:
+        Nq, Nk = s.shape[-2:]
+        s = np.where(np.arange(Nk)[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    return p / p.sum(-1, keepdims=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_stored_output_equal_to_exact_output_changes_nothing(causal):
+    """Given the exact forward output, the row term rowsum(dO * O) equals rowsum(P * dP), so the
+    gradients are those of the chain rule (page "flash_attention_2.cu", backward kernel: D from
+    the stored output)."""
+    q, k, v, g = rand((2, 2, 6, 5), 71), rand((2, 2, 8, 5), 72), rand((2, 2, 8, 5), 73), rand((2, 2, 6, 5), 74)
+    o, _ = oracle.attention_fwd(q, k, v, 0.45, causal)
+    for a, b in zip(oracle.attention_bwd(q, k, v, g, 0.45, causal, o=o), oracle.attention_bwd(q, k, v, g, 0.45, causal)):
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_stored_output_perturbation_moves_gradients_by_the_closed_form(causal):
+    """A stored output o + E changes the row term by dD_i = sum_c dO_ic E_ic. dS = P (dP - D) is
+    linear in D, so dQ moves by -scale dD_i sum_j P_ij k_j, dK by -scale sum_i P_ij dD_i q_i,
+    and dV not at all."""
+    scale = 0.6
+    q, k, v, g = rand((1, 2, 7, 4), 81), rand((1, 2, 9, 4), 82), rand((1, 2, 9, 4), 83), rand((1, 2, 7, 4), 84)
+    o, _ = oracle.attention_fwd(q, k, v, scale, causal)
+    e = rand(o.shape, 85, 1e-2)
+    base = oracle.attention_bwd(q, k, v, g, scale, causal, o=o)
+    moved = oracle.attention_bwd(q, k, v, g, scale, causal, o=o + e)
+    p = _probs(q, k, scale, causal)
+    dD = (g * e).sum(-1)  # [B,H,Nq]
+    want_dq = -scale * dD[..., None] * np.einsum("bhqk,bhkd->bhqd", p, k)
+    want_dk = -scale * np.einsum("bhqk,bhq,bhqd->bhkd", p, dD, q)
+    assert np.max(np.abs((moved[0] - base[0]) - want_dq)) < 1e-12
+    assert np.max(np.abs((moved[1] - base[1]) - want_dk)) < 1e-12
+    assert np.max(np.abs(moved[2] - base[2])) < 1e-12

@@ -34,7 +34,9 @@ MUTATIONS = [
     ("fwd: missing division by the row sum", C, "o_row[c] = acc / l;", "o_row[c] = acc;", [FWD]),
     ("fwd: L without the row max", C, "*lse_out = m + log(l);", "*lse_out = log(l);", [FWD]),
     ("fwd: L in base 2", C, "*lse_out = m + log(l);", "*lse_out = m + log2(l);", [FWD]),
-    ("bwd: dropped D term of dS", PY, "ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "ds = p * dp", [BWD]),
+    ("bwd: dropped D term of dS", PY, "ds = p * (dp - D)", "ds = p * dp", [BWD]),
+    ("bwd: row term from the stored output without dO", PY,
+     "D = (do[b, h] * o[b, h]).sum(axis=1, keepdims=True)", "D = o[b, h].sum(axis=1, keepdims=True)", [BWD]),
     ("bwd: missing scale in dQ", PY, "dq[b, h] = scale * (ds @ k[b, h])", "dq[b, h] = ds @ k[b, h]", [BWD]),
     ("bwd: K in place of V in dP", PY, "dp = do[b, h] @ v[b, h].T", "dp = do[b, h] @ k[b, h].T", [BWD]),
     ("bwd: causal mask one key too wide", PY,
