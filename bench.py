@@ -344,6 +344,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="pages_f32")
+    ap.add_argument("--shape", default=None, metavar="B,H,Nq,Nk,d,dtype,causal",
+                    help="time this shape instead of a named workload (seeded N(0,1) inputs; implies --quick), "
+                         "e.g. 4,16,4096,4096,32,bf16,0")
     ap.add_argument("--quick", action="store_true", help="headline only: no other workloads, sweep or CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -378,6 +381,12 @@ def main():
     props = torch.cuda.get_device_properties(0)
 
     w = WORKLOADS[args.workload]
+    if args.shape:
+        from exact_attention_58_amd.workloads import Workload
+        B_, H_, Nq_, Nk_, d_, dt_, c_ = args.shape.split(",")
+        w = Workload(f"shape_{B_}x{H_}x{Nq_}x{Nk_}x{d_}_{dt_}{'_causal' if int(c_) else ''}", int(B_), int(H_),
+                     int(Nq_), int(Nk_), int(d_), dt_, bool(int(c_)), seed=11)
+        args.quick = True
     with_oracle = not args.quick and not args.no_cpu
     log(f"headline {w.name}: {args.warmup} warmup + {args.steps} timed steps")
     torch.cuda.synchronize()

@@ -65,8 +65,8 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (dtype == FA_F32)
         return cfg.waves == 4 && cfg.bc == (dpad > 96 ? 32 : 64) &&
                (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
-    if (cfg.bc != 64) return false;
-    if (cfg.waves == 8) return cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
+    if (cfg.waves == 8) return cfg.bc == 64 && cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
+    if (cfg.bc != (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64)) return false;
     if (cfg.waves != 4) return false;
     if (cfg.br == 128) return true;
     return cfg.br == 64 && dpad <= 128;
@@ -140,13 +140,17 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         if (c.dpad <= 96 && wgs128 < (causal ? 4 : 2) * num_cus && Nk > 2 * c.bc) c.br = 64;
         // Causal grids (tuned on MI355X): the split up to four workgroups per CU, in dispatch
         // groups of 128 (B1 H16 N4096 d64: 402 -> 294 us; B1 H64 N1024: 107 -> 91 us; B1 H40
-        // N1024 d64 split 71.6 -> 63.2 us with groups of 128), and above d = 96 one workgroup
-        // per CU (B1 H64 N1024 d128: 205 -> 174 us; B1 H16 N4096: 786 -> 609 us). Neither
+        // N1024 d64 split 71.6 -> 63.2 us with groups of 128), and above d = 96, for grids of
+        // at most two workgroups per CU, one workgroup per CU (B1 H64 N1024 d128: 205 -> 174
+        // us; B1 H16 N4096: 791 -> 614 us; B4 H16 N1024: 208 -> 175 us); the large grid B4 H16
+        // N4096 (eight per CU) measured 2177 -> 2460 us with it and keeps the default. Neither
         // knob changes a result bit.
         if (causal && c.br == 64) c.group = 128;
-        if (causal && c.dpad > 96) c.occ = 1;
+        if (causal && c.dpad > 96 && wgs128 <= 2 * (int64_t)num_cus) c.occ = 1;
     } else {
-        c.bc = 64;
+        // the 4-wave kernel's key tiles: 128 keys up to d = 32, 32 above d = 224 (register
+        // budget), else 64 (the ping-pong kernel's are 64)
+        c.bc = c.dpad > 224 ? 32 : c.dpad <= 32 ? 128 : 64;
         // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte
         // loads, its grid still gives every compute unit a workgroup and the key loop is
         // long enough for its pipeline to pay off. Short key sequences (<= 512, HBM-bound)
@@ -170,6 +174,7 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
             // (B1 H20 N2048 d64: 46.5 -> 39.7 us; B1 H56 N1024 d128: 41.2 -> 38.1 us)
             c.waves = 8;
             c.br = 256;
+            c.bc = 64;
         } else if (c.dpad <= 128 && (wgs128 < num_cus || (causal && wgs128 < 2 * num_cus)) &&
                    Nk > 2 * c.bc) {
             // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
@@ -374,8 +379,10 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     fa_status st = fa::check_args(dtype, B, H, Nq, Nk, d);
     if (st != FA_OK) return st;
     const int dpad = (int)((d + 31) / 32) * 32;
-    const fa::TileConfig cand[4] = {{256, 64, 8, dpad, 0, 0}, {128, 64, 4, dpad, 0, 0},
-                                    {64, 64, 4, dpad, 0, 0}, {128, dpad > 96 ? 32 : 64, 4, dpad, 0, 0}};
+    // the 4-wave kernels' key tiles for this dtype and head dim
+    const int bcw = dtype == FA_F32 ? (dpad > 96 ? 32 : 64) : (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64);
+    constexpr int kCand = 3;
+    const fa::TileConfig cand[kCand] = {{256, 64, 8, dpad, 0, 0}, {128, bcw, 4, dpad, 0, 0}, {64, bcw, 4, dpad, 0, 0}};
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;
@@ -385,8 +392,8 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     }
     fa_status result = FA_EUNSUPPORTED;
     // one untimed launch each; it also rejects configurations with no kernel for these inputs
-    bool admitted[4] = {false, false, false, false};
-    for (int i = 0; i < 4 && result != FA_ELAUNCH; ++i) {
+    bool admitted[kCand] = {false, false, false};
+    for (int i = 0; i < kCand && result != FA_ELAUNCH; ++i) {
         st = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
                          stream, &cand[i]);
         if (st == FA_OK) {
@@ -412,16 +419,16 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     // until about 20 ms of GPU time have passed. Then two rounds over every admitted
     // configuration; each keeps its faster round.
     int first = 0;
-    while (first < 4 && !admitted[first]) ++first;
+    while (first < kCand && !admitted[first]) ++first;
     float warm_ms = 0.0f;
     for (int n = 0; result == FA_OK && warm_ms < 20.0f && n < 4096; n += 8) {
         const float ms = timed(cand[first], 8);
         if (ms < 0.0f) result = FA_ELAUNCH;
         warm_ms += ms;
     }
-    float best_round[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float best_round[kCand] = {0.0f, 0.0f, 0.0f};
     for (int round = 0; round < 2 && result == FA_OK; ++round)
-        for (int i = 0; i < 4 && result == FA_OK; ++i) {
+        for (int i = 0; i < kCand && result == FA_OK; ++i) {
             if (!admitted[i]) continue;
             const float ms = timed(cand[i], reps);
             if (ms < 0.0f) result = FA_ELAUNCH;
@@ -430,7 +437,7 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     fa::TileConfig best{};
     float best_ms = 0.0f;
     bool have = false;
-    for (int i = 0; i < 4 && result == FA_OK; ++i)
+    for (int i = 0; i < kCand && result == FA_OK; ++i)
         if (admitted[i] && (!have || best_round[i] < best_ms)) {
             best = cand[i];
             best_ms = best_round[i];
@@ -457,7 +464,10 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
             auto pairs_per_group = [&](int slots) {
                 return std::min<int64_t>(per, (slots + n_tiles - 1) / n_tiles);
             };
-            const int builtin = (dtype != FA_F32 && best.waves == 4 && dpad > 128) ? 32 : 64;
+            const int builtin = dtype == FA_F32 || best.waves != 4 ? 64
+                                : dpad > 128                         ? 32
+                                : dpad <= 32 && best.br == 128       ? 96
+                                                                     : 64;
             int64_t seen[5];
             int n_seen = 0;
             seen[n_seen++] = pairs_per_group(builtin);

@@ -215,11 +215,11 @@ __device__ __attribute__((always_inline)) inline float tile_sum(const f32x16 (&s
 // returns the sum of the fp32 weights (a balanced tree). l sums the fp32 weights, not the
 // rounded ones: a 16-bit weight carries up to 2^-8 relative rounding error, which a row with
 // few visible keys would pass straight into L = m + ln(l).
-template <typename T>
-__device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16 (&s)[2], unsigned (&pk)[2][8]) {
-    const float sum = tile_sum<2>(s);
+template <typename T, int NKB>
+__device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16 (&s)[NKB], unsigned (&pk)[NKB][8]) {
+    const float sum = tile_sum<NKB>(s);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
     return sum;
@@ -232,16 +232,24 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 // staged per step); at the end the second half's (O, m, l) pass through LDS and the first
 // half merges them: m = max(m1, m2), l = l1 2^(m1-m) + l2 2^(m2-m), O likewise, the same
 // exact combination the online recurrence makes tile by tile.
+// Head dims up to 32 run 128-key tiles (half the barriers and reductions per key, where the
+// softmax's vector work dominates) and, without the key split, three waves per SIMD.
+template <int DP, int SPLIT>
+constexpr int fwd16_waves_per_simd() { return DP > 128 ? 1 : (DP <= 32 && SPLIT == 1) ? 3 : 2; }
+
 template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DP > 128 ? 1 : 2, DP > 128 ? 1 : 2)))
+                          amdgpu_waves_per_eu(fwd16_waves_per_simd<DP, SPLIT>(), fwd16_waves_per_simd<DP, SPLIT>())))
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
     // Causal grids split too: a workgroup's rows start at q0 = 64 t and its key tiles end at
     // its diagonal, so the second half starts at key 64 ceil((t + 1) / 2) <= q0 and every row
     // sees a key of the first tile it processes (for t = 0 the second half has no tile and
     // merges as zero weight).
     static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
-    constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB, BC = 64;
+    // K/V tiles of 64 keys; 128 up to DP = 32; 32 at DP = 256, where 64-key tiles staged
+    // through registers no longer fit the 512 registers of one wave per SIMD
+    constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB, BC = DP > 224 ? 32 : DP <= 32 ? 128 : 64;
+    constexpr int NKB = BC / 32;
     constexpr int KST = DP + 8;   // K row stride (elements): 16-byte pad, conflict-free b128 reads
     // V row stride: 4 consecutive rows must start in 4 distinct quarters of the 16 bank groups
     // (the transposed read serves 4 rows x 4 chunks at once), i.e. a pitch of 4 or 12 chunks
@@ -266,7 +274,8 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
-    const TileId wt = tile_of(a, n_qtiles, DP > 128 ? 32 : 64);
+    // an XCD holds 32 CUs x (workgroups per CU) of these at once
+    const TileId wt = tile_of(a, n_qtiles, 32 * fwd16_waves_per_simd<DP, SPLIT>());
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
@@ -340,9 +349,9 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
         if (CAUSAL && k0 > r0w + 31) continue;  // every key of the tile is above this wave's rows
 
         // ---- S^T = K Q^T: two 32-key blocks
-        f32x16 s[2];
+        f32x16 s[NKB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
             s[kb] = f32x16{};
             const uint16_t* kp = Ks + (kb * 32 + l32) * KST + 8 * h32;
 #pragma unroll
@@ -354,9 +363,9 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
         // workgroups the products of one take precedence and the other's softmax fills in
         __builtin_amdgcn_s_setprio(0);
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        softmax_step<2, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
-        unsigned pk[2][8];
-        l_run += pack_and_sum<T>(s, pk);
+        softmax_step<NKB, NDB, CAUSAL>(s, oacc, m_run, l_run, c, masked, k0, Nk, myq, h32);
+        unsigned pk[NKB][8];
+        l_run += pack_and_sum<T, NKB>(s, pk);
         __builtin_amdgcn_s_setprio(1);
 
         // ---- O^T += V^T P^T: 4 k-steps of 16 keys

@@ -102,7 +102,9 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
 @pytest.mark.parametrize("cfg,kw", [
     ((256, 64, 8), dict(dtype=0)),             # no fp32 ping-pong kernel
     ((128, 64, 4), dict(dtype=0, d=128)),      # fp32 d > 96 uses 32-key tiles
-    ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys
+    ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys for 32 < d <= 224
+    ((128, 64, 4), dict(dtype=2, d=32)),       # and 128 keys up to d = 32
+    ((64, 64, 4), dict(dtype=1, d=20)),
     ((64, 32, 4), dict(dtype=0, d=128)),       # no fp32 key split above d = 96
     ((64, 64, 4), dict(d=136)),                # the 16-bit key split stops at d = 128
     ((256, 64, 8), dict(d=136)),               # ping-pong only up to d = 128
@@ -172,7 +174,7 @@ def test_bwd_unsupported(L, kw):
 def test_select_config_large_head_dims(dtype, d):
     """Head dims past 128 (16-bit only): the 4-wave kernel compiled for the padded dim."""
     cfg = fa.fa_select_config(dtype, 4, 16, 4096, 4096, d, False)
-    assert cfg["waves"] == 4 and cfg["Br"] == 128 and cfg["Bc"] == 64
+    assert cfg["waves"] == 4 and cfg["Br"] == 128 and cfg["Bc"] == (32 if d > 224 else 64)
     assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
     vpad = 64 if (cfg["dpad"] // 8) % 8 == 0 else 0
     lds = cfg["Bc"] * (cfg["dpad"] * 2 + 16) + cfg["Bc"] * (cfg["dpad"] * 2 + vpad)
@@ -185,7 +187,7 @@ def test_select_config(dtype, d):
     cfg = fa.fa_select_config(dtype, 4, 16, 4096, 4096, d, False)
     assert cfg["dpad"] % 32 == 0 and d <= cfg["dpad"] < d + 32
     assert cfg["Br"] == 32 * cfg["waves"] or (cfg["waves"] == 4 and cfg["Br"] == 64)
-    assert cfg["Bc"] in (32, 64)
+    assert cfg["Bc"] in (32, 64, 128)
     s = 4 if dtype == "f32" else 2
     if cfg["waves"] == 8:
         # ping-pong kernel, one workgroup per CU

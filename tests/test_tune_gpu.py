@@ -22,7 +22,8 @@ pytestmark = pytest.mark.gpu
 TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
 TOL_L = 1e-3
 ALL = [{"Br": 256, "Bc": 64, "waves": 8}, {"Br": 128, "Bc": 64, "waves": 4},
-       {"Br": 64, "Bc": 64, "waves": 4}, {"Br": 128, "Bc": 32, "waves": 4}]
+       {"Br": 64, "Bc": 64, "waves": 4}, {"Br": 128, "Bc": 32, "waves": 4},
+       {"Br": 128, "Bc": 128, "waves": 4}, {"Br": 64, "Bc": 128, "waves": 4}]
 
 
 def say(*a):
@@ -47,11 +48,12 @@ def admitted(dt, d, causal):
         bc = 32 if dpad > 96 else 64
         split = [] if dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}]
         return [{"Br": 128, "Bc": bc, "waves": 4}] + split
-    out = [{"Br": 128, "Bc": 64, "waves": 4}]
+    bc = 32 if dpad > 224 else 128 if dpad <= 32 else 64
+    out = [{"Br": 128, "Bc": bc, "waves": 4}]
     if d % 8 == 0 and dpad <= 128:
         out.append({"Br": 256, "Bc": 64, "waves": 8})
     if dpad <= 128:
-        out.append({"Br": 64, "Bc": 64, "waves": 4})
+        out.append({"Br": 64, "Bc": bc, "waves": 4})
     return out
 
 
@@ -67,6 +69,8 @@ CASES = [
     ("f16", 2, 2, 257, 513, 128, False), ("f16", 1, 2, 129, 1000, 96, False),
     ("bf16", 1, 1, 200, 200, 200, True), ("bf16", 1, 2, 100, 90, 40, False),
     ("f32", 1, 2, 300, 700, 64, False), ("f32", 1, 1, 100, 300, 128, True),
+    ("bf16", 1, 2, 200, 300, 256, False), ("f16", 1, 1, 150, 170, 250, True),
+    ("bf16", 1, 2, 300, 700, 32, True), ("f16", 2, 2, 257, 513, 24, False), ("f32", 1, 2, 200, 300, 32, True),
 ]
 
 
