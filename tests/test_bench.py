@@ -73,7 +73,9 @@ def test_roofline_fields_and_traffic_key():
     # traffic is reported only for the kernel source it was measured on
     assert bench.roofline_for(w, ms, recorded["kernel_sha"])["traffic"] == recorded["bytes"]
     assert bench.roofline_for(w, ms, "0" * 16)["traffic"] is None
-    assert bench.roofline_for(WORKLOADS["ragged_f16"], ms, sha)["traffic"] is None
+    # a workload without a profile reports none
+    assert bench.roofline_for(w.with_(name="shape_not_profiled"), ms, sha)["traffic"] is None
+    assert set(bench.TRAFFIC) == set(WORKLOADS)  # every named workload has its counters
 
 
 def test_kernel_sha_covers_the_forward_sources():
