@@ -65,7 +65,7 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (dtype == FA_F32)
         return cfg.waves == 4 && cfg.bc == (dpad > 96 ? 32 : 64) &&
                (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
-    if (cfg.waves == 8) return cfg.bc == 64 && cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
+    if (cfg.waves == 8) return cfg.bc == pp_keys(dpad) && cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
     if (cfg.bc != (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64)) return false;
     if (cfg.waves != 4) return false;
     if (cfg.br == 128) return true;
@@ -149,7 +149,7 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         if (causal && c.dpad > 96 && wgs128 <= 2 * (int64_t)num_cus) c.occ = 1;
     } else {
         // the 4-wave kernel's key tiles: 128 keys up to d = 32, 32 above d = 224 (register
-        // budget), else 64 (the ping-pong kernel's are 64)
+        // budget), else 64 (the ping-pong kernel's: 128 up to d = 64, else 64)
         c.bc = c.dpad > 224 ? 32 : c.dpad <= 32 ? 128 : 64;
         // Two-group ping-pong kernel (8 waves, 256 rows) when the inputs allow 16-byte
         // loads, its grid still gives every compute unit a workgroup and the key loop is
@@ -158,29 +158,34 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // (bf16 d=128, N=128: 4.7 vs 2.8 TB/s on MI355X). Causal grids keep the 4-wave
         // kernel longer: its 128-row tiles waste less on the diagonal and its shorter
         // workgroups balance better. Measured crossover (bf16, MI355X): 2048 keys for
-        // d > 64 (d=128, N=1024: 628 vs 551 TFLOP/s; N=4096: 834 vs 914), 4096 keys for
-        // d <= 64 (N=3072: 587 vs 517; N=16384: 719 vs 793). Head dims up to 32 stay on the
+        // d > 64 (d=128, N=1024: 628 vs 551 TFLOP/s; N=4096: 834 vs 914), 2560 keys for
+        // d <= 64 (B4 H32: N=2560 4-wave 162 vs 181 us; N=3072 ping-pong 221 vs 239 us; N=4096
+        // 342 vs 376 us). Causal grids of at most two 128-row workgroups per CU take the key
+        // split below instead when d <= 96 (at two per CU: B1 H8 N8192 d64 split 111,
+        // ping-pong 134, 4-wave 145 us; B2 H8 N4096 d96 83 / 91 / 99 us), not at d = 128
+        // (B1 H16 N4096: ping-pong 105, split 111 us). Head dims up to 32 stay on the
         // 4-wave kernel at every length: with four exp2 per MFMA both kernels are bound by
         // the softmax's vector work, and the smaller workgroups do it faster (d=32, N=4096:
         // 575 vs 515 TFLOP/s).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
-        const int64_t pp_min_keys = !causal ? 512 : d <= 64 ? 4096 : 2048;
+        const int64_t pp_min_keys = !causal ? 512 : d <= 64 ? 2560 : 2048;
+        const bool causal_split = causal && wgs128 <= 2 * (int64_t)num_cus;
         if (d > 128) {
             // head dims past 128: the 4-wave kernel, one wave per SIMD
         } else if (aligned && d % 8 == 0 && d > 32 && wgs256 * 8 >= (int64_t)num_cus * (causal ? 8 : 5) &&
-                   Nk > pp_min_keys) {
+                   Nk > pp_min_keys && !(causal_split && c.dpad <= 96)) {
             // non-causal grids keep the ping-pong kernel down to 5/8 of a workgroup per CU
             // (B1 H20 N2048 d64: 46.5 -> 39.7 us; B1 H56 N1024 d128: 41.2 -> 38.1 us)
             c.waves = 8;
             c.br = 256;
-            c.bc = 64;
-        } else if (c.dpad <= 128 && (wgs128 < num_cus || (causal && wgs128 < 2 * num_cus)) &&
-                   Nk > 2 * c.bc) {
+            c.bc = pp_keys(c.dpad);
+        } else if (c.dpad <= 128 && (wgs128 < num_cus || causal_split) && Nk > 2 * c.bc) {
             // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
             // block's keys walked in two halves by two waves and merged at the end. Causal
             // grids split up to two workgroups per CU: their uneven workgroups leave a tail
-            // that the split halves (B1 H20 N2048 d64 causal: 46.1 -> 33.2 us). Non-causal
+            // that the split halves (B1 H20 N2048 d64 causal: 46.1 -> 33.2 us; at two per CU,
+            // B1 H16 N4096 d64: 77 -> 64 us, B1 H32 N2048 d64: 42 -> 38 us). Non-causal
             // grids between one and two per CU measured slower split (B1 H56 N1024 d128:
             // 45.4 vs 59.9 us).
             c.br = 64;
@@ -382,7 +387,7 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     // the 4-wave kernels' key tiles for this dtype and head dim
     const int bcw = dtype == FA_F32 ? (dpad > 96 ? 32 : 64) : (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64);
     constexpr int kCand = 3;
-    const fa::TileConfig cand[kCand] = {{256, 64, 8, dpad, 0, 0}, {128, bcw, 4, dpad, 0, 0}, {64, bcw, 4, dpad, 0, 0}};
+    const fa::TileConfig cand[kCand] = {{256, fa::pp_keys(dpad), 8, dpad, 0, 0}, {128, bcw, 4, dpad, 0, 0}, {64, bcw, 4, dpad, 0, 0}};
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;

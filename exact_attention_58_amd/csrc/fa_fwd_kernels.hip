@@ -443,6 +443,18 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
 
 // ---------------------------------------------------------------- 16-bit, two-group ping-pong
 
+// Reduction op r of an in-place pairwise tree over P values (levels of P/2, P/4, ..., 1 ops
+// in that order): the slot it writes, part[o] = part[2o] + part[2o+1].
+template <int P>
+constexpr int tree_slot(int r) {
+    int base = 0;
+    for (int n = P / 2; n >= 1; n /= 2) {
+        if (r < base + n) return r - base;
+        base += n;
+    }
+    return 0;
+}
+
 // LDS row pitches. The LDS serves 256 bytes per clock over 64 four-byte banks, i.e. 16 bank
 // groups of 16 bytes; a b128 read is served 16 lanes at a time and a 64-bit transposed read 32
 // lanes at a time. K fragments read 16 consecutive rows at one 16-byte chunk: an odd pitch (in
@@ -477,11 +489,15 @@ template <int DP> struct Pitch {
 // the first one multiplies a zero P by the resident V_0, and a causal wave past its diagonal
 // runs fully masked tiles whose weights are exactly zero; the phases are barrier-bound, so
 // neither costs time.
+// Key tiles hold 64 keys, and 128 up to DP = 64: there a 64-key phase is short (16 MFMAs),
+// and the longer tile halves the barriers, row-max reductions and rescale tests per key
+// (about 7% faster at d = 64; three K and four V buffers of 128 keys take 150 KB of LDS).
 template <typename T, int DP, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     constexpr int WPG = 4, NWAVE = 2 * WPG;
-    constexpr int BR = 32 * NWAVE, BC = 64;
+    constexpr int BR = 32 * NWAVE, BC = pp_keys(DP);
+    constexpr int NKB = BC / 32;
     constexpr int DCH = DP / 8;                    // 16-byte data chunks per row
     constexpr int KP = Pitch<DP>::K, VP = Pitch<DP>::V;
     constexpr int KTILEB = BC * KP * 16, VTILEB = BC * VP * 16;
@@ -526,20 +542,21 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int dchunks = d / 8;
 
     // Direct HBM->LDS copy of the K and V tiles into rows of KP / VP chunks. The copy of a
-    // tile pair is KP + VP wave instructions (64 lanes x 16 B, wave-uniform LDS destination,
+    // tile pair is KI + VI wave instructions (64 lanes x 16 B, wave-uniform LDS destination,
     // lane i -> +16*i); instruction c = it*NWAVE + wave belongs to this wave. A lane on a
     // padding chunk loads a valid chunk of its row into the padding, which is never read, so
     // the copy of a full tile needs no lane mask. Chunks past d (DP > d) repeat the row's last
     // data chunk: finite, and Q is zero there, so they add nothing to the scores. A tile that
     // runs past Nk repeats row Nk-1 in its tail rows (finite; their scores are masked and
     // their weights are zero); only that last tile takes the slower clamped path.
-    constexpr int NCP = (KP + VP + NWAVE - 1) / NWAVE;
+    constexpr int KI = KP * BC / 64, VI = VP * BC / 64;  // copy instructions per K / V tile
+    constexpr int NCP = (KI + VI + NWAVE - 1) / NWAVE;
     unsigned coff[NCP];  // lane's byte offset within a full tile (row r, column chunk)
 #pragma unroll
     for (int it = 0; it < NCP; ++it) {
         const int c = it * NWAVE + wave;
-        const int pitch = c < KP ? KP : VP;
-        const int idx = c < KP ? c : c - KP;
+        const int pitch = c < KI ? KP : VP;
+        const int idx = c < KI ? c : c - KI;
         const int p = idx * 64 + lane;
         const int r = p / pitch, cch = p - r * pitch;
         coff[it] = (unsigned)(r * d + min(cch, dchunks - 1) * 8) * 2u;
@@ -549,9 +566,9 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     // copy instruction `it` of this wave for tile m (wave-uniform branches only)
     auto issue_copy = [&](int it, int m) __attribute__((always_inline)) {
         const int c = it * NWAVE + wave;
-        if (m >= n || c >= KP + VP) return;
-        const bool isk = c < KP;
-        const int idx = isk ? c : c - KP;
+        if (m >= n || c >= KI + VI) return;
+        const bool isk = c < KI;
+        const int idx = isk ? c : c - KI;
         const uint8_t* tile = (const uint8_t*)((isk ? kg : vg) + (int64_t)m * BC * d);
         uint8_t* dst = (isk ? kbuf(m) : vbuf(m)) + idx * 1024;
         if (m * BC + BC <= Nk) {
@@ -576,10 +593,10 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
     float m_run = kNegInf, l_run = 0.0f;
     const float c = a.scale_log2;
-    f32x16 s[2];
-    unsigned pk[2][8];
+    f32x16 s[NKB];
+    unsigned pk[NKB][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pk[0][i] = pk[1][i] = 0u;
+    for (int i = 0; i < 8 * NKB; ++i) pk[i / 8][i % 8] = 0u;
 
     // MFMA phase as one unrolled micro-program: NQ MFMAs of S^T_j = K_j Q^T (k-step ds of key
     // block kb) then NP MFMAs of O^T += V_{j-1}^T P_{j-1}^T (key step t of head-dim block db).
@@ -587,7 +604,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     // barriers keep that order, so the one wave of this group on the SIMD keeps the matrix
     // core fed while the LDS reads of the next MFMAs are in flight. A QK operand is one b128
     // read, a PV operand two transposed b64 reads: at most 2*LA LDS reads are outstanding.
-    constexpr int NQ = 2 * NDS, NP = (BC / 16) * NDB;
+    constexpr int NQ = NKB * NDS, NP = (BC / 16) * NDB;
     constexpr int LA = 6;
     const int i16 = lane & 15, g16 = (lane >> 4) & 1;
     // per-lane operand bases (LDS byte addresses); every fragment is base + compile-time offset
@@ -605,7 +622,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
             const u32x2 hi = lds_rdtr16<off + 8 * VP * 16>(va);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
-            constexpr int qi = i - NP, ds = qi >> 1, kb = qi & 1;
+            constexpr int qi = i - NP, ds = qi / NKB, kb = qi % NKB;
             return lds_rd128<kb * 32 * KP * 16 + ds * 32>(ka);
         }
     };
@@ -623,7 +640,8 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     // DO_PV: accumulate P V of tile jp (its first LA operands already in the ring);
     // DO_QK: compute S^T_j. Both compile-time so the unrolled program and its ring are static.
     // partial sums of the previous tile's weights (tree folded around the MFMAs)
-    float part[16];
+    constexpr int NPART = 8 * NKB;  // pair sums of the tile's 16 NKB weights
+    float part[NPART];
     auto mphase_t = [&](auto do_qk_c, auto do_pv_c, int j, int jp) __attribute__((always_inline)) {
         constexpr bool DO_QK = decltype(do_qk_c)::value, DO_PV = decltype(do_pv_c)::value;
         static_assert(DO_PV, "the MFMA phase always folds the previous tile's weights");
@@ -654,20 +672,20 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
                                   pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
                 oacc[db] = Half<T>::mfma(op, pb, oacc[db]);
                 // first tree level of the previous tile's weight sum (s still holds them):
-                // pair q of the 16 is added at PV step q mod NP
-                static_for<0, 16>([&](auto qc) __attribute__((always_inline)) {
+                // pair q of the NPART is added at PV step q mod NP
+                static_for<0, NPART>([&](auto qc) __attribute__((always_inline)) {
                     constexpr int q = decltype(qc)::value;
                     if constexpr (q % NP == i) part[q] = s[q >> 3][2 * (q & 7)] + s[q >> 3][2 * (q & 7) + 1];
                 });
             } else {
-                constexpr int qi = i - NP, ds = qi >> 1, kb = qi & 1;
+                constexpr int qi = i - NP, ds = qi / NKB, kb = qi % NKB;
                 // the first k-step of each key block starts from a zero accumulator
                 s[kb] = Half<T>::mfma(op, qf[ds], ds == 0 ? f32x16{} : s[kb]);
-                // remaining tree levels (8, 4, 2, 1 partial sums = reduction ops 0..14, in
-                // dependency order), spread over the NQ QK steps
-                static_for<(qi * 15) / NQ, ((qi + 1) * 15) / NQ>([&](auto rc) __attribute__((always_inline)) {
+                // remaining tree levels (NPART / 2, ..., 2, 1 partial sums = reduction ops
+                // 0..NPART-2, in dependency order), spread over the NQ QK steps
+                static_for<(qi * (NPART - 1)) / NQ, ((qi + 1) * (NPART - 1)) / NQ>([&](auto rc) __attribute__((always_inline)) {
                     constexpr int r = decltype(rc)::value;
-                    constexpr int o = r < 8 ? r : r < 12 ? r - 8 : r < 14 ? r - 12 : 0;
+                    constexpr int o = tree_slot<NPART>(r);
                     part[o] = part[2 * o] + part[2 * o + 1];
                 });
             }
@@ -675,7 +693,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
         });
         if constexpr (!DO_QK) {
 #pragma unroll
-            for (int n2 = 8; n2 >= 1; n2 /= 2)
+            for (int n2 = NPART / 2; n2 >= 1; n2 /= 2)
 #pragma unroll
                 for (int i = 0; i < n2; ++i) part[i] = part[2 * i] + part[2 * i + 1];
         }
@@ -687,12 +705,12 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     auto tile_max = [&](int j) __attribute__((always_inline)) {
         const int k0 = j * BC;
         const bool masked = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > r0w);
-        mt = tile_max_log2<2, CAUSAL>(s, c, masked, k0, Nk, myq, h32, &cc);
+        mt = tile_max_log2<NKB, CAUSAL>(s, c, masked, k0, Nk, myq, h32, &cc);
     };
     auto softmax = [&]() __attribute__((always_inline)) {
-        tile_exp<2, NDB>(s, oacc, m_run, l_run, mt, cc);
+        tile_exp<NKB, NDB>(s, oacc, m_run, l_run, mt, cc);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(s[kb][r], s[kb][r + 1]);
     };
@@ -704,7 +722,7 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     __syncthreads();
     prefetch_pv(0);  // operands of the first (zero-weight) PV product
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[0][i] = s[1][i] = 0.0f;  // no previous tile to fold into l
+    for (int i = 0; i < 16 * NKB; ++i) s[i / 16][i % 16] = 0.0f;  // no previous tile to fold into l
 
     const bool g0 = grp == 0;
     if (!g0) barrier_nofence();  // group 1 starts one phase later

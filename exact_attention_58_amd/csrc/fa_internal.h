@@ -38,6 +38,9 @@ struct TileConfig {
     int group;  // FwdArgs::slots for causal grids (8..1024); 0: the kernel's own
 };
 
+// Keys per K/V tile of the 16-bit ping-pong kernel for a padded head dim.
+constexpr int pp_keys(int dpad) { return dpad <= 64 ? 128 : 64; }
+
 // Pure selection logic (no HIP calls). Returns 0 on success, 2 if no kernel fits.
 // `aligned`: all buffers 16-byte aligned and d*element_size a multiple of 16.
 int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,

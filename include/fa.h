@@ -136,7 +136,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  *
  * Br, Bc, waves: query rows per workgroup, keys per K/V tile and waves per workgroup, as
  * fa_select_config and fa_tune_fwd report them. The kernels that exist: for fp16/bf16,
- * (256, 64, 8) when every buffer is 16-byte aligned, d % 8 == 0 and d <= 128; the 4-wave kernel
+ * the ping-pong kernel (256, Bc, 8) with Bc = 128 keys for d <= 64 and 64 above, when every
+ * buffer is 16-byte aligned, d % 8 == 0 and d <= 128; the 4-wave kernel
  * (128, Bc, 4) and its two-way key split (64, Bc, 4, d <= 128), with Bc = 128 keys for
  * d <= 32, 32 for d > 224 and 64 otherwise. For fp32, (128, 64, 4) for d <= 96 and
  * (128, 32, 4) above, and (64, 64, 4) when d <= 96. Any other triple returns
@@ -286,13 +287,14 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  * compute-unit count `num_cus` (<= 0 means 256), with no HIP call at all, so that the rules
  * can be checked for any device on a machine without one. Also writes the padded head
  * dimension the kernel is compiled for (*dpad, a multiple of 32). The rules:
- *  - fp16/bf16: the two-group ping-pong kernel (256 rows, 8 waves) for aligned rows with
- *    d % 8 == 0 and 32 < d <= 128, when its grid has at least 5/8 of a workgroup per CU
- *    (one per CU for causal grids) and the key length passes the crossover (more than 512
- *    keys; causal: more than 2048, or 4096 for d <= 64); otherwise the 4-wave kernel
- *    (128 rows; 128-key tiles up to d = 32, 32-key tiles above d = 224), or its two-way key
- *    split (64 rows, d <= 128) for grids of fewer 128-row workgroups than CUs (than two per
- *    CU for causal grids).
+ *  - fp16/bf16: the two-group ping-pong kernel (256 rows, 8 waves; 128-key tiles up to
+ *    d = 64, 64-key tiles above) for aligned rows with d % 8 == 0 and 32 < d <= 128, when
+ *    its grid has at least 5/8 of a workgroup per CU (one per CU for causal grids) and the
+ *    key length passes the crossover (more than 512 keys; causal: more than 2048, or 2560
+ *    for d <= 64), except causal grids with d <= 96 and at most two 128-row workgroups per
+ *    CU; otherwise the 4-wave kernel (128 rows; 128-key tiles up to d = 32, 32-key tiles
+ *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of fewer 128-row
+ *    workgroups than CUs (at most two per CU for causal grids).
  *  - fp32: one 4-wave kernel per head dim (128 rows; 64-key tiles up to d = 96, 32-key
  *    tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
  *    (four per CU for causal grids).

@@ -108,8 +108,10 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
     ((64, 32, 4), dict(dtype=0, d=128)),       # no fp32 key split above d = 96
     ((64, 64, 4), dict(d=136)),                # the 16-bit key split stops at d = 128
     ((256, 64, 8), dict(d=136)),               # ping-pong only up to d = 128
-    ((256, 64, 8), dict(d=60)),                # and for d % 8 == 0
-    ((256, 64, 8), dict(q=P + 2)),             # and for 16-byte aligned rows
+    ((256, 128, 8), dict(d=60)),               # and for d % 8 == 0
+    ((256, 128, 8), dict(q=P + 2)),            # and for 16-byte aligned rows
+    ((256, 64, 8), dict(d=64)),                # ping-pong tiles: 128 keys up to d = 64
+    ((256, 128, 8), dict(d=96)),               # and 64 keys above
     ((512, 64, 16), dict()), ((128, 64, 8), dict()), ((0, 0, 0), dict()),
     ((128, 64, 4), dict(occ=5)), ((128, 64, 4), dict(occ=-1)),       # knob ranges
     ((128, 64, 4), dict(group=4)), ((128, 64, 4), dict(group=2048)),
@@ -211,7 +213,9 @@ def test_select_config(dtype, d):
 def test_select_config_grid_fill(dtype):
     """The 256-row kernel only when its grid gives every compute unit a workgroup."""
     big = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 128, False, num_cus=256)
-    assert big["waves"] == 8 and big["Br"] == 256
+    assert big["waves"] == 8 and big["Br"] == 256 and big["Bc"] == 64
+    big64 = fa.fa_select_config(dtype, 4, 16, 4096, 4096, 64, False, num_cus=256)
+    assert big64["waves"] == 8 and big64["Bc"] == 128  # 128-key tiles up to d = 64
     small = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, False, num_cus=256)
     # too few 128-row workgroups: 64 rows per workgroup, keys split between two waves
     assert small["waves"] == 4 and small["Br"] == 64
@@ -224,6 +228,13 @@ def test_select_config_grid_fill(dtype):
     assert fa.fa_select_config(dtype, 1, 16, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
     assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["waves"] == 4
     assert fa.fa_select_config(dtype, 1, 40, 2048, 2048, 64, True, num_cus=256)["Br"] == 128
+    # causal grids of exactly two 128-row workgroups per CU: the key split up to d = 96, the
+    # ping-pong kernel at d = 128; three per CU: the ping-pong kernel
+    assert fa.fa_select_config(dtype, 1, 16, 4096, 4096, 64, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 8, 8192, 8192, 64, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 2, 8, 4096, 4096, 96, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 16, 4096, 4096, 128, True, num_cus=256)["waves"] == 8
+    assert fa.fa_select_config(dtype, 1, 32, 3072, 3072, 64, True, num_cus=256)["waves"] == 8
     small_d128 = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 128, False, num_cus=256)
     assert small_d128["Br"] == 64  # the key split reaches d = 128 for 16-bit inputs
     # enough 128-row workgroups (d % 8 != 0 keeps the 256-row kernel out): no key split
@@ -241,8 +252,8 @@ def test_select_config_grid_fill(dtype):
     # head dims up to 32: the 4-wave kernel at every length
     for causal in (False, True):
         assert fa.fa_select_config(dtype, 4, 16, 16384, 16384, 32, causal, num_cus=256)["waves"] == 4
-    # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 4096 keys (d <= 64)
-    for d, last_4wave in ((128, 2048), (96, 2048), (64, 4096)):
+    # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 2560 keys (d <= 64)
+    for d, last_4wave in ((128, 2048), (96, 2048), (64, 2560)):
         at = fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, True, num_cus=256)
         past = fa.fa_select_config(dtype, 4, 32, last_4wave + 1, last_4wave + 1, d, True, num_cus=256)
         assert at["waves"] == 4 and past["waves"] == 8, (d, at, past)

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
 TOL_L = 1e-3
-ALL = [{"Br": 256, "Bc": 64, "waves": 8}, {"Br": 128, "Bc": 64, "waves": 4},
+ALL = [{"Br": 256, "Bc": 64, "waves": 8}, {"Br": 256, "Bc": 128, "waves": 8}, {"Br": 128, "Bc": 64, "waves": 4},
        {"Br": 64, "Bc": 64, "waves": 4}, {"Br": 128, "Bc": 32, "waves": 4},
        {"Br": 128, "Bc": 128, "waves": 4}, {"Br": 64, "Bc": 128, "waves": 4}]
 
@@ -51,7 +51,7 @@ def admitted(dt, d, causal):
     bc = 32 if dpad > 224 else 128 if dpad <= 32 else 64
     out = [{"Br": 128, "Bc": bc, "waves": 4}]
     if d % 8 == 0 and dpad <= 128:
-        out.append({"Br": 256, "Bc": 64, "waves": 8})
+        out.append({"Br": 256, "Bc": 128 if dpad <= 64 else 64, "waves": 8})
     if dpad <= 128:
         out.append({"Br": 64, "Bc": bc, "waves": 4})
     return out
