@@ -7,7 +7,8 @@
 // That page accumulates dQ with atomic adds from a loop over key tiles; here three kernels
 // share the work without atomics:
 //  * row terms: D = rowsum(dO * O) per query row (fp32, into a caller's workspace);
-//  * dK, dV: one workgroup per 128 keys (4 waves x 32), looping over query tiles of 64;
+//  * dK, dV: one workgroup per 128 keys, looping over query tiles of 64 (4 waves x 32 keys
+//    up to d = 96; above, 8 waves in two roles that split each 32-key block's products);
 //  * dQ: one workgroup per 128 queries (4 waves x 32), looping over key tiles of 64.
 // Both tile kernels recompute S and dP on MFMA 32x32x16 (16-bit operands, fp32 accumulate);
 // P and dS are rounded to the input type for the products that consume them.
@@ -91,26 +92,25 @@ void bwd_delta_any_kernel(const void* o, const void* dout, float* delta, int64_t
 
 // Tile of 64 rows x DP columns (16-bit) staged through registers into LDS rows of STR
 // elements; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0, aligned).
-template <int DP, int STR, bool VEC>
+template <int DP, int STR, bool VEC, int NT = 256>
 struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
-    static constexpr int CH = 64 * CPR / 256;         // chunks per thread
-    static_assert(64 * CPR % 256 == 0, "tile split");
+    static constexpr int CH = (64 * CPR + NT - 1) / NT;  // chunks per thread (the last maybe partial)
     u32x4 r[CH];
     __device__ __attribute__((always_inline)) void load(const uint16_t* base, int row0, int nrows, int d, int tid) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 256;
+            const int chunk = tid + c * NT;
             const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
+            if (64 * CPR % NT == 0 || chunk < 64 * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
         }
     }
     __device__ __attribute__((always_inline)) void store(uint16_t* lds, int tid) const {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 256;
+            const int chunk = tid + c * NT;
             const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            *(u32x4*)(lds + row * STR + col) = r[c];
+            if (64 * CPR % NT == 0 || chunk < 64 * CPR) *(u32x4*)(lds + row * STR + col) = r[c];
         }
     }
 };
@@ -129,16 +129,12 @@ __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* t
 
 // ---------------------------------------------------------------- dK, dV
 
-// MODE 0 computes dK and dV together; MODE 1 only dV (S, P, P^T dO) and MODE 2 only dK
-// (S, dP, dS, dS^T Q), which recompute S each but hold half the accumulators. Two waves
-// share a SIMD whenever the registers fit (up to d = 96 for MODE 0, every d for the single
-// modes): one wave's LDS reads and staged loads then overlap the other's products, about
-// 1.5x the throughput of one wave per SIMD.
-template <typename T, int DP, bool CAUSAL, int MODE, bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(DP <= 96 || MODE != 0 ? 2 : 1, DP <= 96 || MODE != 0 ? 2 : 1)))
+// dK and dV together for d <= 96, two waves per SIMD: one wave's LDS reads and staged loads
+// then overlap the other's products, about 1.5x the throughput of one wave per SIMD.
+template <typename T, int DP, bool CAUSAL, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
-    constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
+    static_assert(DP <= 96, "above d = 96: bwd_dkdv_pair_kernel");
     constexpr int BK = 128, BQ = 64;  // keys per workgroup, queries per tile
     constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
     constexpr int NDS = DP / 16, NDB = DP / 32;
@@ -169,7 +165,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
         kf[ds] = load_chunk16<VEC>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
-        if constexpr (DO_DK) vf[ds] = load_chunk16<VEC>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
+        vf[ds] = load_chunk16<VEC>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
     }
 
     f32x16 dva[NDB], dka[NDB];
@@ -215,7 +211,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
                 s = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], s);
-                if constexpr (DO_DK) dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+                dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
             }
             // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey. The weight is
             // kept iff off = 8 (r/4) + r%4 >= lo: lo puts the causal diagonal (q >= mykey) in
@@ -228,23 +224,18 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
             for (int g = 0; g < 4; ++g) {
                 const int ql = qb * 32 + 8 * g + 4 * h32;
                 const f32x4 lv = *(const f32x4*)(Ls + ql);
-                f32x4 dv = {};
-                if constexpr (DO_DK) dv = *(const f32x4*)(Ds + ql);
+                const f32x4 dv = *(const f32x4*)(Ds + ql);
                 float pv[4], sv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float p = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
                     pv[e] = p;
-                    if constexpr (DO_DK) sv[e] = p * (dp[4 * g + e] - dv[e]);
+                    sv[e] = p * (dp[4 * g + e] - dv[e]);
                 }
-                if constexpr (DO_DV) {
-                    ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
-                    ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
-                }
-                if constexpr (DO_DK) {
-                    spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
-                    spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
-                }
+                ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
+                spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
             }
             // dV += P^T dO and dK += dS^T Q over the two 16-query steps of this block
 #pragma unroll
@@ -253,14 +244,10 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                 const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    if constexpr (DO_DV) {
-                        const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
-                        dva[db] = Half<T>::mfma(pa, gb, dva[db]);
-                    }
-                    if constexpr (DO_DK) {
-                        const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
-                        dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
-                    }
+                    const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
+                    dva[db] = Half<T>::mfma(pa, gb, dva[db]);
+                    const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
+                    dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
                 }
             }
         }
@@ -278,10 +265,215 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
         for (int r = 0; r < 16; ++r) {
             const int key = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
             if (key < Nk) {
-                if constexpr (DO_DV) dvg[(int64_t)key * d + col] = Half<T>::one(dva[db][r]);
-                if constexpr (DO_DK) dkg[(int64_t)key * d + col] = Half<T>::one(dka[db][r] * sc);
+                dvg[(int64_t)key * d + col] = Half<T>::one(dva[db][r]);
+                dkg[(int64_t)key * d + col] = Half<T>::one(dka[db][r] * sc);
             }
         }
+    }
+}
+
+
+// dK and dV for d > 96, with the products of each 32-key block on two waves that share a
+// SIMD. Wave w < KB (role A) computes S = Q K^T, P and dV += P^T dO; wave w + KB (role B)
+// computes dP = dO V^T and, from the P that role A passes through LDS in fp32, dS = P (dP - D)
+// and dK += dS^T Q. Each holds half the accumulators and resident key fragments of the fused
+// kernel, so both fit two waves per SIMD, and S is computed once (separate dV and dK kernels
+// would each compute it). The gradients are those of the fused kernel bit for bit. The query loop runs in
+// steps of 32 queries; B handles step i - 1 while A handles step i, so neither waits for the
+// other within a step, and a workgroup barrier ends each step. Query tiles (64 rows of Q and
+// dO, with L and D) have two LDS buffers: tile t is read in steps 2t..2t+2 and tile t+2 is
+// stored into the same buffer in step 2t+3; its loads are issued two steps earlier and stay
+// in flight across the barriers (a plain s_barrier after an LDS-only wait).
+template <typename T, int DP, bool CAUSAL, bool VEC>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
+    constexpr int KB = 4;  // key blocks of 32 per workgroup (one per SIMD)
+    constexpr int NT = 128 * KB;
+    constexpr int BK = 32 * KB, BQ = 64;
+    constexpr int STR = DP + 8;
+    constexpr int NDS = DP / 16, NDB = DP / 32;
+    __shared__ __attribute__((aligned(16))) uint16_t Qsb[2][BQ * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t Gsb[2][BQ * STR];  // dO
+    __shared__ __attribute__((aligned(16))) float Lsb[2][BQ];
+    __shared__ __attribute__((aligned(16))) float Dsb[2][BQ];
+    // P of one step per key block, [buffer][key block][register group][lane]: lane-contiguous
+    // 16-byte rows, so the writes and reads of a register group are conflict-free
+    __shared__ __attribute__((aligned(16))) f32x4 Pb[2][KB][4][64];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h32 = lane >> 5, l32 = lane & 31;
+    const int kbk = wave % KB;
+    // one workgroup per CU: an XCD holds 32 at once
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, 32);
+    const int bh = pt.pair, kt = pt.tile;
+    const int Nq = a.Nq, Nk = a.Nk, d = a.d;
+    const int k0 = kt * BK;
+    const int kw0 = k0 + 32 * kbk;
+    const int mykey = kw0 + l32;
+
+    const uint16_t* qg = (const uint16_t*)a.q + (int64_t)bh * Nq * d;
+    const uint16_t* kg = (const uint16_t*)a.k + (int64_t)bh * Nk * d;
+    const uint16_t* vg = (const uint16_t*)a.v + (int64_t)bh * Nk * d;
+    const uint16_t* gg = (const uint16_t*)a.dout + (int64_t)bh * Nq * d;
+    const float* lg = a.lse + (int64_t)bh * Nq;
+    const float* dg = a.delta + (int64_t)bh * Nq;
+    const float c = a.scale_log2;
+
+    // query tiles that see any key of this workgroup (causal: queries >= k0)
+    const int qt0 = CAUSAL ? k0 / BQ : 0;
+    const int nt = max((Nq + BQ - 1) / BQ - qt0, 0);
+    const int n_steps = nt > 0 ? 2 * nt + 1 : 0;
+    TileCopy<DP, STR, VEC, NT> qc, gc;
+    float lrow = 0.0f, drow = 0.0f;
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
+        const int r0 = (qt0 + t) * BQ;
+        qc.load(qg, r0, Nq, d, tid);
+        gc.load(gg, r0, Nq, d, tid);
+        if (tid < BQ) {
+            const int q = r0 + tid;
+            lrow = q < Nq ? lg[q] * kLog2e : 0.0f;
+            drow = q < Nq ? dg[q] : 0.0f;
+        }
+    };
+    auto store_tile = [&](int b) __attribute__((always_inline)) {
+        qc.store(Qsb[b], tid);
+        gc.store(Gsb[b], tid);
+        if (tid < BQ) {
+            Lsb[b][tid] = lrow;
+            Dsb[b][tid] = drow;
+        }
+    };
+    if (nt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    if (nt > 1) {
+        load_tile(1);
+        store_tile(1);
+    }
+    if (nt > 2) load_tile(2);
+    __syncthreads();
+    // LDS writes of this step done, then the workgroup barrier; loads stay in flight
+    auto end_step = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // tile staging of step s (every wave): tile t = (s + 1) / 2 into its buffer at odd s >= 3,
+    // then the loads of tile t + 1
+    auto stage = [&](int s) __attribute__((always_inline)) {
+        if (s >= 3 && (s & 1)) {
+            const int t = (s + 1) >> 1;
+            if (t < nt) {
+                store_tile(t & 1);
+                if (t + 1 < nt) load_tile(t + 1);
+            }
+        }
+    };
+    // step index i -> (tile, 32-query block); a causal step whose queries all precede the
+    // wave's keys is skipped by both roles alike
+    auto step_active = [&](int i) __attribute__((always_inline)) {
+        return !(CAUSAL && (qt0 + (i >> 1)) * BQ + (i & 1) * 32 + 31 < kw0);
+    };
+    uint16_t* dkg = (uint16_t*)a.dk + (int64_t)bh * Nk * d;
+    uint16_t* dvg = (uint16_t*)a.dv + (int64_t)bh * Nk * d;
+    // register r of block db: key kw0 + 8 (r/4) + 4 h32 + r%4, column db*32 + l32
+    auto write_grad = [&](uint16_t* out, const f32x16 (&acc)[NDB], float sc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int col = db * 32 + l32;
+            if (col >= d) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kw0 + 8 * (r >> 2) + 4 * h32 + (r & 3);
+                if (key < Nk) out[(int64_t)key * d + col] = Half<T>::one(acc[db][r] * sc);
+            }
+        }
+    };
+
+    if (wave < KB) {
+        // role A: S, P, dV
+        u32x4 kf[NDS];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kf[ds] = load_chunk16<VEC>(kg, mykey, ds * 16 + 8 * h32, Nk, d);
+        f32x16 dva[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) dva[i] = f32x16{};
+        for (int s = 0; s < n_steps; ++s) {
+            stage(s);
+            if (s < 2 * nt && step_active(s)) {
+                const int b = (s >> 1) & 1, qb = s & 1;
+                const int qbase = (qt0 + (s >> 1)) * BQ + qb * 32;
+                const uint16_t* qp = Qsb[b] + (qb * 32 + l32) * STR + 8 * h32;
+                f32x16 sacc = f32x16{};
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) sacc = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], sacc);
+                // register r: query qbase + 8 (r/4) + 4 h32 + r%4, key mykey; kept iff
+                // 8 (r/4) + r%4 >= lo (key past Nk: none; causal: on or below the diagonal).
+                // Padded query rows need no test: their Q, dO and L are zero, and their weight
+                // of 1 meets dO = 0 (and dP - D = 0 in role B).
+                const int lo = mykey >= Nk ? 64 : CAUSAL ? mykey - qbase - 4 * h32 : -64;
+                unsigned ppk[8];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 lv = *(const f32x4*)(Lsb[b] + qb * 32 + 8 * g + 4 * h32);
+                    f32x4 pv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pv[e] = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + e], c, -lv[e])) : 0.0f;
+                    Pb[s & 1][kbk][g][lane] = pv;
+                    ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                    ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4 pa = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        dva[db] = Half<T>::mfma(pa, tr_frag<STR>(Gsb[b], qb * 32 + 16 * t, db * 32, lane), dva[db]);
+                }
+            }
+            end_step();
+        }
+        write_grad(dvg, dva, 1.0f);
+    } else {
+        // role B, one step behind: dP, dS, dK
+        u32x4 vf[NDS];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) vf[ds] = load_chunk16<VEC>(vg, mykey, ds * 16 + 8 * h32, Nk, d);
+        f32x16 dka[NDB];
+#pragma unroll
+        for (int i = 0; i < NDB; ++i) dka[i] = f32x16{};
+        for (int s = 0; s < n_steps; ++s) {
+            stage(s);
+            const int i = s - 1;
+            if (i >= 0 && step_active(i)) {
+                const int b = (i >> 1) & 1, qb = i & 1;
+                const uint16_t* gp = Gsb[b] + (qb * 32 + l32) * STR + 8 * h32;
+                f32x16 dp = f32x16{};
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+                unsigned spk[8];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 dv = *(const f32x4*)(Dsb[b] + qb * 32 + 8 * g + 4 * h32);
+                    const f32x4 pv = Pb[i & 1][kbk][g][lane];
+                    float sv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sv[e] = pv[e] * (dp[4 * g + e] - dv[e]);
+                    spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
+                    spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        dka[db] = Half<T>::mfma(sa, tr_frag<STR>(Qsb[b], qb * 32 + 16 * t, db * 32, lane), dka[db]);
+                }
+            }
+            end_step();
+        }
+        write_grad(dkg, dka, a.scale);
     }
 }
 
@@ -455,7 +647,9 @@ __device__ __attribute__((always_inline)) inline void load_half_row(float (&dst)
 // dO read from LDS along the head dim), so a lane holds one key and 16 queries; register r of
 // S is then, with the queries of the reduction enumerated in accumulator order, the A operand
 // of dV += P^T dO (and dS of dK += dS^T Q), whose B operand is one dO (Q) row element per lane
-// read from LDS. MODE as in the 16-bit kernel (0: dK and dV, 1: dV only, 2: dK only).
+// read from LDS. MODE 0 computes dK and dV, MODE 1 only dV (S, P, P^T dO) and MODE 2 only dK
+// (S, dP, dS, dS^T Q): above d = 64 the two single-gradient kernels each recompute S but hold
+// half the accumulators.
 template <int DP, bool CAUSAL, int MODE, bool VEC>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(DP <= 64 || MODE == 1 ? 2 : 1, DP <= 64 || MODE == 1 ? 2 : 1)))
@@ -758,18 +952,16 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
     if constexpr (DP <= 96) {
         if (a.causal)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
         else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 0, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
     } else {
-        // dV and dK as two kernels that each fit two waves per SIMD
-        if (a.causal) {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
-        } else {
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 1, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, 2, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
-        }
+        // above d = 96 the accumulators of both gradients no longer fit one wave at two waves
+        // per SIMD: the two-role kernel, 128 keys per workgroup
+        if (a.causal)
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, DP, true, VEC>), dim3(g1), dim3(512), 0, st, a, n_kt);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, DP, false, VEC>), dim3(g1), dim3(512), 0, st, a, n_kt);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
