@@ -35,6 +35,8 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 // workgroups an XCD holds at once: 32 CUs x two 4-wave workgroups (two waves per SIMD)
 constexpr int kXcdSlots = 64;
 
@@ -97,12 +99,38 @@ struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
     static constexpr int CH = (64 * CPR + NT - 1) / NT;  // chunks per thread (the last maybe partial)
     u32x4 r[CH];
-    __device__ __attribute__((always_inline)) void load(const uint16_t* base, int row0, int nrows, int d, int tid) {
+    // VEC: byte offset of this thread's chunk within a tile, or an offset past any buffer
+    // (a chunk past d, or a thread without a chunk) that the load's range check turns into 0
+    unsigned voff[CH];
+    __device__ __attribute__((always_inline)) void init(int d, int tid) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * NT;
-            const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            if (64 * CPR % NT == 0 || chunk < 64 * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * NT;
+                const int row = chunk / CPR, col = (chunk % CPR) * 8;
+                const bool ok = (64 * CPR % NT == 0 || chunk < 64 * CPR) && col < d;
+                voff[c] = ok ? (unsigned)(row * d + col) * 2u : 0x80000000u;
+            }
+        }
+    }
+    // VEC: buffer loads over rows [row0, nrows) of the tensor, so rows past nrows read as
+    // zeros by the hardware's range check, without a branch per chunk
+    __device__ __attribute__((always_inline)) void load(const uint16_t* base, int row0, int nrows, int d, int tid) {
+        if constexpr (VEC) {
+            const int64_t rem = (int64_t)(nrows - row0) * d * 2;
+            const int nbytes = rem <= 0 ? 0 : rem > 0x7fffffff ? 0x7fffffff : (int)rem;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)row0 * d), (short)0, nbytes, kBufferFlags);
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                r[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
+        } else {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * NT;
+                const int row = chunk / CPR, col = (chunk % CPR) * 8;
+                if (64 * CPR % NT == 0 || chunk < 64 * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
+            }
         }
     }
     __device__ __attribute__((always_inline)) void store(uint16_t* lds, int tid) const {
@@ -177,6 +205,8 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
     TileCopy<DP, STR, VEC> qc, gc;
+    qc.init(d, tid);
+    gc.init(d, tid);
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int qt) __attribute__((always_inline)) {
         qc.load(qg, qt * BQ, Nq, d, tid);
@@ -219,24 +249,36 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
             // rows (q >= Nq) need no test: their Q, dO, L and D are zero, so the weight
             // exp2(0) = 1 meets dO = 0 and dP - D = 0 and adds nothing.
             const int lo = mykey >= Nk ? 64 : CAUSAL ? mykey - q0 - qb * 32 - 4 * h32 : -64;
+            // every weight of the block kept (all keys below Nk, all queries on or past the
+            // diagonal): the wave skips the compares
+            const bool full = kw0 + 32 <= Nk && (!CAUSAL || kw0 + 31 <= q0 + qb * 32);
             unsigned ppk[8], spk[8];
+            auto weights = [&](auto masked_c) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int ql = qb * 32 + 8 * g + 4 * h32;
-                const f32x4 lv = *(const f32x4*)(Ls + ql);
-                const f32x4 dv = *(const f32x4*)(Ds + ql);
-                float pv[4], sv[4];
+                for (int g = 0; g < 4; ++g) {
+                    const int ql = qb * 32 + 8 * g + 4 * h32;
+                    const f32x4 lv = *(const f32x4*)(Ls + ql);
+                    const f32x4 dv = *(const f32x4*)(Ds + ql);
+                    float pv[4], sv[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e])) : 0.0f;
-                    pv[e] = p;
-                    sv[e] = p * (dp[4 * g + e] - dv[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const float p = !MASKED || 8 * g + e >= lo
+                                            ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * g + e], c, -lv[e]))
+                                            : 0.0f;
+                        pv[e] = p;
+                        sv[e] = p * (dp[4 * g + e] - dv[e]);
+                    }
+                    ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                    ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                    spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
+                    spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
                 }
-                ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
-                ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
-                spk[2 * g] = Half<T>::pack2(sv[0], sv[1]);
-                spk[2 * g + 1] = Half<T>::pack2(sv[2], sv[3]);
-            }
+            };
+            // (the unmasked copy only for 16-byte rows: the element-wise instances have no
+            // registers to spare for it)
+            if (VEC && full) weights(std::false_type{});
+            else weights(std::true_type{});
             // dV += P^T dO and dK += dS^T Q over the two 16-query steps of this block
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -325,6 +367,8 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
     const int nt = max((Nq + BQ - 1) / BQ - qt0, 0);
     const int n_steps = nt > 0 ? 2 * nt + 1 : 0;
     TileCopy<DP, STR, VEC, NT> qc, gc;
+    qc.init(d, tid);
+    gc.init(d, tid);
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int r0 = (qt0 + t) * BQ;
@@ -412,18 +456,26 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
                 // Padded query rows need no test: their Q, dO and L are zero, and their weight
                 // of 1 meets dO = 0 (and dP - D = 0 in role B).
                 const int lo = mykey >= Nk ? 64 : CAUSAL ? mykey - qbase - 4 * h32 : -64;
+                const bool full = kw0 + 32 <= Nk && (!CAUSAL || kw0 + 31 <= qbase);
                 unsigned ppk[8];
+                auto weights = [&](auto masked_c) __attribute__((always_inline)) {
+                    constexpr bool MASKED = decltype(masked_c)::value;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 lv = *(const f32x4*)(Lsb[b] + qb * 32 + 8 * g + 4 * h32);
-                    f32x4 pv;
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 lv = *(const f32x4*)(Lsb[b] + qb * 32 + 8 * g + 4 * h32);
+                        f32x4 pv;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pv[e] = 8 * g + e >= lo ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + e], c, -lv[e])) : 0.0f;
-                    Pb[s & 1][kbk][g][lane] = pv;
-                    ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
-                    ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
-                }
+                        for (int e = 0; e < 4; ++e)
+                            pv[e] = !MASKED || 8 * g + e >= lo
+                                        ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[4 * g + e], c, -lv[e]))
+                                        : 0.0f;
+                        Pb[s & 1][kbk][g][lane] = pv;
+                        ppk[2 * g] = Half<T>::pack2(pv[0], pv[1]);
+                        ppk[2 * g + 1] = Half<T>::pack2(pv[2], pv[3]);
+                    }
+                };
+                if (full) weights(std::false_type{});
+                else weights(std::true_type{});
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const u32x4 pa = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
@@ -525,6 +577,8 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
     TileCopy<DP, STR, VEC> kc, vc;
+    kc.init(d, tid);
+    vc.init(d, tid);
     kc.load(kg, 0, Nk, d, tid);
     vc.load(vg, 0, Nk, d, tid);
     for (int j = 0; j < n_tiles; ++j) {
@@ -553,15 +607,23 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
                 dp = Half<T>::mfma(*(const u32x4*)(vp + ds * 16), gf[ds], dp);
             }
             const int lim = (CAUSAL ? min(Nk - 1, myq) : Nk - 1) - k0 - kb * 32 - 4 * h32;
-            float sv[16];
+            // every key of the block below Nk and (causal) at or before every query of the wave
+            const bool full = k0 + kb * 32 + 32 <= Nk && (!CAUSAL || k0 + kb * 32 + 31 <= r0w);
+            auto weights = [&](auto masked_c) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked_c)::value;
+                float sv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int off = 8 * (r >> 2) + (r & 3);
-                const float p = off <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq)) : 0.0f;
-                sv[r] = p * (dp[r] - dq);
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int off = 8 * (r >> 2) + (r & 3);
+                    const float p = !MASKED || off <= lim ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lq)) : 0.0f;
+                    sv[r] = p * (dp[r] - dq);
+                }
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(sv[r], sv[r + 1]);
+                for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(sv[r], sv[r + 1]);
+            };
+            // (the unmasked copy only up to d = 96: at d = 128 it does not fit the registers)
+            if (DP <= 96 && VEC && full) weights(std::false_type{});
+            else weights(std::true_type{});
         }
         // dQ^T += K^T dS^T: four 16-key steps
 #pragma unroll
