@@ -35,8 +35,6 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
-// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format, no swizzle).
-constexpr int kBufferFlags = 0x00020000;
 // workgroups an XCD holds at once: 32 CUs x two 4-wave workgroups (two waves per SIMD)
 constexpr int kXcdSlots = 64;
 
@@ -109,7 +107,7 @@ struct TileCopy {
                 const int chunk = tid + c * NT;
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
                 const bool ok = (64 * CPR % NT == 0 || chunk < 64 * CPR) && col < d;
-                voff[c] = ok ? (unsigned)(row * d + col) * 2u : 0x80000000u;
+                voff[c] = ok ? (unsigned)(row * d + col) * 2u : kBufferVoid;
             }
         }
     }
@@ -117,13 +115,9 @@ struct TileCopy {
     // zeros by the hardware's range check, without a branch per chunk
     __device__ __attribute__((always_inline)) void load(const uint16_t* base, int row0, int nrows, int d, int tid) {
         if constexpr (VEC) {
-            const int64_t rem = (int64_t)(nrows - row0) * d * 2;
-            const int nbytes = rem <= 0 ? 0 : rem > 0x7fffffff ? 0x7fffffff : (int)rem;
-            const __amdgpu_buffer_rsrc_t rs =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)row0 * d), (short)0, nbytes, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base + (int64_t)row0 * d, (int64_t)(nrows - row0) * d * 2);
 #pragma unroll
-            for (int c = 0; c < CH; ++c)
-                r[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
+            for (int c = 0; c < CH; ++c) r[c] = buffer_load16(rs, voff[c]);
         } else {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {

@@ -158,6 +158,21 @@ __device__ inline unsigned lds_addr(const void* p) {
     return (unsigned)(uintptr_t)(const FA_LDS void*)(p);
 }
 
+// Raw buffer resource over the `nbytes` bytes at p (clamped to [0, 2^31 - 1]): loads through
+// it at byte offsets past nbytes return zeros without touching memory (the buffer range
+// check), so a tile that runs past the end of a tensor needs no per-chunk branch. Word 3 is
+// the gfx9-family format (32-bit data, no swizzle); p, nbytes must be wave-uniform.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, int64_t nbytes) {
+    const int n = nbytes <= 0 ? 0 : nbytes > 0x7fffffff ? 0x7fffffff : (int)nbytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, n, 0x00020000);
+}
+// An offset past any range buffer_rsrc makes: its loads return zeros.
+constexpr unsigned kBufferVoid = 0x80000000u;
+// 16 bytes at byte offset `off` of a buffer resource (zeros past its range).
+__device__ inline u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // One 16-byte chunk (8 elements) of row `row`, columns [col, col+8), zero outside
 // [0, nrows) x [0, ncols). VEC: rows are 16-byte aligned and ncols % 8 == 0.
 template <bool VEC>

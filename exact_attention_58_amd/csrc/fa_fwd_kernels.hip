@@ -302,19 +302,40 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     // key half h walks tiles [h * n_steps, min(n_tiles, (h + 1) * n_steps))
     const int n_steps = (n_tiles + SPLIT - 1) / SPLIT;
 
-    // step i stages tile h * n_steps + i of every half h (rows past Nk load as zeros)
+    // step i stages tile h * n_steps + i of every half h (rows past Nk load as zeros). With
+    // 16-byte rows the chunks load through buffer resources that end at row Nk (or hold
+    // nothing for a tile past the last), at per-thread offsets fixed for every tile.
     u32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
+    unsigned voff[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const int chunk = tid + c * 64 * NW;
+        const int row = chunk / CPR, col = (chunk % CPR) * 8;
+        voff[c] = col < d ? (unsigned)(row * d + col) * 2u : kBufferVoid;
+    }
     auto load_tile = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < SPLIT; ++h)
+        for (int h = 0; h < SPLIT; ++h) {
+            const int j = h * n_steps + i;
+            if constexpr (VEC) {
+                const int64_t nb = j < n_tiles ? (int64_t)(Nk - j * BC) * d * 2 : 0;
+                const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (int64_t)j * BC * d, nb);
+                const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (int64_t)j * BC * d, nb);
 #pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * 64 * NW;
-                const int row = chunk / CPR, col = (chunk % CPR) * 8;
-                const int j = h * n_steps + i;
-                kreg[h][c] = load_chunk16<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
-                vreg[h][c] = load_chunk16<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+                for (int c = 0; c < CH; ++c) {
+                    kreg[h][c] = buffer_load16(rk, voff[c]);
+                    vreg[h][c] = buffer_load16(rv, voff[c]);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int chunk = tid + c * 64 * NW;
+                    const int row = chunk / CPR, col = (chunk % CPR) * 8;
+                    kreg[h][c] = load_chunk16<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+                    vreg[h][c] = load_chunk16<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+                }
             }
+        }
     };
     auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -835,15 +856,35 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    // staging of SPLIT tiles (one per key half; rows past Nk load as zeros)
+    // staging of SPLIT tiles (one per key half; rows past Nk load as zeros). With 16-byte
+    // rows the chunks load through buffer resources that end at row Nk (or hold nothing for
+    // a tile past the last), at per-thread offsets fixed for every tile.
     f32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
-    auto load_tile_h = [&](int h, int j) __attribute__((always_inline)) {
+    unsigned voff[CH];
 #pragma unroll
-        for (int cc = 0; cc < CH; ++cc) {
-            const int chunk = tid + cc * 64 * NW;
-            const int row = chunk / CPR, col = (chunk % CPR) * 4;
-            kreg[h][cc] = load_chunk32<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
-            vreg[h][cc] = load_chunk32<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+    for (int cc = 0; cc < CH; ++cc) {
+        const int chunk = tid + cc * 64 * NW;
+        const int row = chunk / CPR, col = (chunk % CPR) * 4;
+        voff[cc] = col < d ? (unsigned)(row * d + col) * 4u : kBufferVoid;
+    }
+    auto load_tile_h = [&](int h, int j) __attribute__((always_inline)) {
+        if constexpr (VEC) {
+            const int64_t nb = j < n_tiles ? (int64_t)(Nk - j * BC) * d * 4 : 0;
+            const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + (int64_t)j * BC * d, nb);
+            const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vg + (int64_t)j * BC * d, nb);
+#pragma unroll
+            for (int cc = 0; cc < CH; ++cc) {
+                kreg[h][cc] = __builtin_bit_cast(f32x4, buffer_load16(rk, voff[cc]));
+                vreg[h][cc] = __builtin_bit_cast(f32x4, buffer_load16(rv, voff[cc]));
+            }
+        } else {
+#pragma unroll
+            for (int cc = 0; cc < CH; ++cc) {
+                const int chunk = tid + cc * 64 * NW;
+                const int row = chunk / CPR, col = (chunk % CPR) * 4;
+                kreg[h][cc] = load_chunk32<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+                vreg[h][cc] = load_chunk32<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
+            }
         }
     };
     auto store_tile_h = [&](int h, int b) __attribute__((always_inline)) {
