@@ -813,10 +813,11 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NKB = BC / 32;
     constexpr int NDB = DP / 32;
 
-    // Two K/V buffers when two workgroups still fit the CU's 160 KiB of LDS: tile j+1 is
-    // stored while tile j is read, one barrier per tile. Otherwise one buffer, two barriers.
-    // The key split keeps one buffer per half.
-    constexpr int NBUF = SPLIT == 2 || 2 * 2 * BC * (KST + VST) * 4 <= 160 * 1024 ? 2 : 1;
+    // One K/V buffer per key half, two barriers per tile: tile j+1 is stored once every wave
+    // has read tile j, and its loads are in flight while tile j is computed. (Two buffers with
+    // one barrier per tile, where two workgroups still fit the LDS, measured slower: fp32 B4
+    // H4 N4096 d64 524 vs 504 us, d128 994 vs 980 us, causal B1 H16 N4096 d128 595 vs 588 us.)
+    constexpr int NBUF = SPLIT;
     __shared__ __attribute__((aligned(16))) float Ks[NBUF][BC * KST];
     __shared__ __attribute__((aligned(16))) float Vs[NBUF][BC * VST];
     static_assert(SPLIT == 1 || RB * (NDB * 16 + 2) * 64 <= NBUF * BC * KST, "merge fits the K buffers");
@@ -989,19 +990,6 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
             for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a1 + mrg[(db * 16 + r) * 64 + lane] * a2;
         l_run = l_run * a1 + l2 * a2;
         m_run = m;
-    } else if constexpr (NBUF == 2) {
-        load_tile(0);
-        store_tile(0);
-        __syncthreads();
-        if (n_tiles > 1) load_tile(1);
-        for (int j = 0; j < n_tiles; ++j) {
-            tile(j, Ks[j & 1], Vs[j & 1]);
-            // tile j+1 goes to the other buffer, whose last readers (tile j-1) passed the
-            // previous barrier; this barrier publishes it and retires buffer j & 1
-            if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-            __syncthreads();
-            if (j + 2 < n_tiles) load_tile(j + 2);
-        }
     } else {
         load_tile(0);
         for (int j = 0; j < n_tiles; ++j) {
