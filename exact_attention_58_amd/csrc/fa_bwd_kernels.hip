@@ -666,12 +666,29 @@ struct TileCopy32 {
     static constexpr int CH = ROWS * CPR / 256;         // chunks per thread
     static_assert(ROWS * CPR % 256 == 0, "tile split");
     f32x4 r[CH];
-    __device__ __attribute__((always_inline)) void load(const float* base, int row0, int nrows, int d, int tid) {
+    unsigned voff[CH];  // VEC: byte offset of this thread's chunk in a tile (as in TileCopy)
+    __device__ __attribute__((always_inline)) void init(int d, int tid) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 256;
-            const int row = chunk / CPR, col = (chunk % CPR) * 4;
-            r[c] = load_chunk32<VEC>(base, row0 + row, col, nrows, d);
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * 256;
+                const int row = chunk / CPR, col = (chunk % CPR) * 4;
+                voff[c] = col < d ? (unsigned)(row * d + col) * 4u : kBufferVoid;
+            }
+        }
+    }
+    __device__ __attribute__((always_inline)) void load(const float* base, int row0, int nrows, int d, int tid) {
+        if constexpr (VEC) {
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base + (int64_t)row0 * d, (int64_t)(nrows - row0) * d * 4);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) r[c] = __builtin_bit_cast(f32x4, buffer_load16(rs, voff[c]));
+        } else {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int chunk = tid + c * 256;
+                const int row = chunk / CPR, col = (chunk % CPR) * 4;
+                r[c] = load_chunk32<VEC>(base, row0 + row, col, nrows, d);
+            }
         }
     }
     __device__ __attribute__((always_inline)) void store(float* lds, int tid) const {
@@ -749,6 +766,8 @@ void bwd32_dkdv_kernel(BwdArgs a, int n_ktiles) {
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
     TileCopy32<BQ, DP, STR, VEC> qc, gc;
+    qc.init(d, tid);
+    gc.init(d, tid);
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int qt) __attribute__((always_inline)) {
         qc.load(qg, qt * BQ, Nq, d, tid);
@@ -887,6 +906,8 @@ void bwd32_dq_kernel(BwdArgs a, int n_qtiles) {
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
     TileCopy32<BC, DP, STR, VEC> kc, vc;
+    kc.init(d, tid);
+    vc.init(d, tid);
     kc.load(kg, 0, Nk, d, tid);
     vc.load(vg, 0, Nk, d, tid);
     for (int j = 0; j < n_tiles; ++j) {
