@@ -63,7 +63,7 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (cfg.occ < 0 || cfg.occ > 4) return false;
     if (cfg.group != 0 && (cfg.group < 8 || cfg.group > 1024)) return false;
     if (dtype == FA_F32)
-        return cfg.waves == 4 && cfg.bc == (dpad > 96 ? 32 : 64) &&
+        return cfg.waves == 4 && cfg.bc == f32_keys(dpad, cfg.br, aligned) &&
                (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
     if (cfg.waves == 8) return cfg.bc == pp_keys(dpad) && cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
     if (cfg.bc != (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64)) return false;
@@ -147,6 +147,9 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // knob changes a result bit.
         if (causal && c.br == 64) c.group = 128;
         if (causal && c.dpad > 96 && wgs128 <= 2 * (int64_t)num_cus) c.occ = 1;
+        // 128-key tiles for 128-row workgroups up to d = 64 over 16-byte rows (fp32 B4 H4
+        // N4096 d64: 505 -> 499.5 us; d32: 270 -> 267 us)
+        c.bc = f32_keys(c.dpad, c.br, aligned);
     } else {
         // the 4-wave kernel's key tiles: 128 keys up to d = 32, 32 above d = 224 (register
         // budget), else 64 (the ping-pong kernel's: 128 up to d = 64, else 64)
@@ -385,9 +388,13 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     if (st != FA_OK) return st;
     const int dpad = (int)((d + 31) / 32) * 32;
     // the 4-wave kernels' key tiles for this dtype and head dim
-    const int bcw = dtype == FA_F32 ? (dpad > 96 ? 32 : 64) : (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64);
+    const int esz = dtype == FA_F32 ? 4 : 2;
+    const bool aligned = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) && (d * esz) % 16 == 0;
+    const int bc16 = dpad > 224 ? 32 : dpad <= 32 ? 128 : 64;
+    const int bc128 = dtype == FA_F32 ? fa::f32_keys(dpad, 128, aligned) : bc16;
+    const int bc64 = dtype == FA_F32 ? fa::f32_keys(dpad, 64, aligned) : bc16;
     constexpr int kCand = 3;
-    const fa::TileConfig cand[kCand] = {{256, fa::pp_keys(dpad), 8, dpad, 0, 0}, {128, bcw, 4, dpad, 0, 0}, {64, bcw, 4, dpad, 0, 0}};
+    const fa::TileConfig cand[kCand] = {{256, fa::pp_keys(dpad), 8, dpad, 0, 0}, {128, bc128, 4, dpad, 0, 0}, {64, bc64, 4, dpad, 0, 0}};
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;

@@ -1107,6 +1107,12 @@ static int launch32(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
                        : launch(fwd32_kernel<DP, BC, false, false, 2>, a, 64, st, 256, cfg.occ);
         }
     }
+    if constexpr (DP <= 64) {
+        if (cfg.bc == 128) {  // 128-key tiles (16-byte rows: checked by the caller)
+            if (a.causal) return launch(fwd32_kernel<DP, 128, true, true, 1>, a, 128, st, 256, cfg.occ);
+            return launch(fwd32_kernel<DP, 128, false, true, 1>, a, 128, st, 256, cfg.occ);
+        }
+    }
     if (a.causal) {
         return vec ? launch(fwd32_kernel<DP, BC, true, true, 1>, a, 128, st, 256, cfg.occ)
                    : launch(fwd32_kernel<DP, BC, true, false, 1>, a, 128, st, 256, cfg.occ);

@@ -139,9 +139,10 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  * the ping-pong kernel (256, Bc, 8) with Bc = 128 keys for d <= 64 and 64 above, when every
  * buffer is 16-byte aligned, d % 8 == 0 and d <= 128; the 4-wave kernel
  * (128, Bc, 4) and its two-way key split (64, Bc, 4, d <= 128), with Bc = 128 keys for
- * d <= 32, 32 for d > 224 and 64 otherwise. For fp32, (128, 64, 4) for d <= 96 and
- * (128, 32, 4) above, and (64, 64, 4) when d <= 96. Any other triple returns
- * FA_EUNSUPPORTED before any HIP call.
+ * d <= 32, 32 for d > 224 and 64 otherwise. For fp32, (128, 128, 4) for d <= 64 when every
+ * buffer is 16-byte aligned and d % 4 == 0, otherwise (128, 64, 4) for d <= 96; (128, 32, 4)
+ * above d = 96; and (64, 64, 4) when d <= 96. Any other triple returns FA_EUNSUPPORTED
+ * before any HIP call.
  * Two knobs change only where and when workgroups run, never a result bit:
  *  - occ (0..4): at most occ workgroups on one CU at a time, by reserving unused LDS
  *    (160 KB / occ per workgroup); 0 = as many as the registers and LDS allow.
@@ -176,7 +177,7 @@ fa_status fa_fwd_config(const void* q, const void* k, const void* v, void* o, fl
  * *group (each may be NULL) and remembered for this
  * exact problem (current device, dtype, B, H, Nq, Nk, d, causal). Later fa_fwd calls on the
  * same problem launch it instead of the built-in choice, as long as the buffers allow it
- * (a ping-pong choice needs 16-byte aligned buffers). The record holds up to 256 problems;
+ * (a ping-pong or 128-key fp32 choice needs 16-byte aligned buffers). The record holds up to 256 problems;
  * beyond that the oldest is replaced.
  *
  * q, k, v, o, lse, sizes, scale, causal, dtype, stream: as for fa_fwd. On FA_OK, o and lse
@@ -274,8 +275,8 @@ const char* fa_status_str(fa_status s);
  * (once per device, cached); with no device visible it assumes MI355X's 256. It is
  * fa_select_config_cus with that count and the padded head dimension dropped. The answer
  * assumes 16-byte aligned buffers; fa_fwd on unaligned buffers (or a 16-bit d that is not a
- * multiple of 8) uses the 4-wave, 128-row kernel, and a configuration recorded by
- * fa_tune_fwd for the same problem replaces it.
+ * multiple of 8) uses the 4-wave, 128-row kernel (for fp32 with 64-key tiles up to d = 96),
+ * and a configuration recorded by fa_tune_fwd for the same problem replaces it.
  *
  * Errors: FA_EINVAL / FA_EUNSUPPORTED exactly as fa_fwd for the same sizes and dtype.
  */
@@ -295,8 +296,8 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    CU; otherwise the 4-wave kernel (128 rows; 128-key tiles up to d = 32, 32-key tiles
  *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of fewer 128-row
  *    workgroups than CUs (at most two per CU for causal grids).
- *  - fp32: one 4-wave kernel per head dim (128 rows; 64-key tiles up to d = 96, 32-key
- *    tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
+ *  - fp32: one 4-wave kernel per head dim (128 rows; 128-key tiles up to d = 64, 64-key
+ *    tiles up to d = 96, 32-key tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
  *    (four per CU for causal grids).
  * The scheduling knobs of fa_fwd_config that the built-in rules set (dispatch groups of 128
  * for the causal fp32 key split, and one workgroup per CU for causal fp32 grids above d = 96

@@ -102,6 +102,10 @@ def call_cfg(L, cfg, q=P, B=1, H=1, Nq=8, Nk=8, d=64, causal=0, dtype=2, scale=0
 @pytest.mark.parametrize("cfg,kw", [
     ((256, 64, 8), dict(dtype=0)),             # no fp32 ping-pong kernel
     ((128, 64, 4), dict(dtype=0, d=128)),      # fp32 d > 96 uses 32-key tiles
+    ((128, 64, 4), dict(dtype=0)),             # fp32 up to d = 64: 128-key tiles on 16-byte rows
+    ((128, 128, 4), dict(dtype=0, q=P + 4)),   # and 64-key tiles on rows off 16-byte alignment
+    ((128, 128, 4), dict(dtype=0, d=96)),      # 128-key fp32 tiles only up to d = 64
+    ((64, 128, 4), dict(dtype=0)),             # and not for the key split
     ((128, 32, 4), dict(dtype=2)),             # 16-bit tiles are 64 keys for 32 < d <= 224
     ((128, 64, 4), dict(dtype=2, d=32)),       # and 128 keys up to d = 32
     ((64, 64, 4), dict(dtype=1, d=20)),

@@ -47,7 +47,9 @@ def admitted(dt, d, causal):
     if dt == "f32":
         bc = 32 if dpad > 96 else 64
         split = [] if dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}]
-        return [{"Br": 128, "Bc": bc, "waves": 4}] + split
+        # 128-key tiles for 128-row workgroups up to d = 64 (16-byte rows: d % 4 == 0)
+        bc128 = 128 if dpad <= 64 and d % 4 == 0 else bc
+        return [{"Br": 128, "Bc": bc128, "waves": 4}] + split
     bc = 32 if dpad > 224 else 128 if dpad <= 32 else 64
     out = [{"Br": 128, "Bc": bc, "waves": 4}]
     if d % 8 == 0 and dpad <= 128:
