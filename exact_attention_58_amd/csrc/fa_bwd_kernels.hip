@@ -615,8 +615,8 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(sv[r], sv[r + 1]);
             };
-            // (the unmasked copy only up to d = 96: at d = 128 it does not fit the registers)
-            if (DP <= 96 && VEC && full) weights(std::false_type{});
+            // (the unmasked copy not for causal d = 128, where it does not fit the registers)
+            if ((DP <= 96 || !CAUSAL) && VEC && full) weights(std::false_type{});
             else weights(std::true_type{});
         }
         // dQ^T += K^T dS^T: four 16-key steps
