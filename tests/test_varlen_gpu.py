@@ -99,6 +99,15 @@ def test_varlen_pingpong_kernel(causal):
     run_case("bf16", 16, lq, lq, 128, causal, seed=41, heads=[0, 15], expect_waves=8)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_pingpong_kernel_128_key_tiles(causal):
+    """d = 64: the ping-pong kernel's 128-key tiles over packed sequences, most of them ending
+    in a partial tile. The longest sequence passes 2560 keys, where causal grids at d <= 64
+    leave the 4-wave kernel."""
+    lq = [2700, 700, 513, 1, 999, 256, 0, 130]
+    run_case("bf16", 16, lq, lq, 64, causal, seed=53, heads=[0, 15], expect_waves=8)
+
+
 def test_varlen_key_split_kernel():
     """A small non-causal grid at d <= 96: the 64-row kernel with the two-way key split."""
     run_case("f16", 2, [300, 200], [700, 129], 64, False, seed=43, expect_waves=4)
