@@ -203,6 +203,12 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
 
 namespace {
 
+// Whether the forward's buffers allow 16-byte row accesses: q, k, v, o 16-byte aligned and rows
+// of a multiple of 16 bytes.
+bool fwd_rows_aligned(const void* q, const void* k, const void* v, const void* o, int64_t d, int esz) {
+    return (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) && (d * esz) % 16 == 0;
+}
+
 fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
                   const int32_t* cu_k, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t tq,
                   int64_t tk, int64_t d, float scale, int causal, fa_dtype dtype, void* stream,
@@ -211,8 +217,7 @@ fa_status run_fwd(const void* q, const void* k, const void* v, void* o, float* l
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % esz != 0 ||
         (uintptr_t)lse % 4 != 0)
         return FA_EINVAL;
-    const bool vec = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) &&
-                     (d * esz) % 16 == 0;
+    const bool vec = fwd_rows_aligned(q, k, v, o, d, esz);
     if (force && !config_ok(*force, dtype, d, causal, vec)) return FA_EUNSUPPORTED;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
@@ -389,7 +394,7 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     const int dpad = (int)((d + 31) / 32) * 32;
     // the 4-wave kernels' key tiles for this dtype and head dim
     const int esz = dtype == FA_F32 ? 4 : 2;
-    const bool aligned = (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % 16 == 0) && (d * esz) % 16 == 0;
+    const bool aligned = fa::fwd_rows_aligned(q, k, v, o, d, esz);
     const int bc16 = dpad > 224 ? 32 : dpad <= 32 ? 128 : 64;
     const int bc128 = dtype == FA_F32 ? fa::f32_keys(dpad, 128, aligned) : bc16;
     const int bc64 = dtype == FA_F32 ? fa::f32_keys(dpad, 64, aligned) : bc16;
