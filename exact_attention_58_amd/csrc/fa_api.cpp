@@ -275,6 +275,8 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     if (d > kMaxDim32) return FA_EUNSUPPORTED;
     const bool vec = all % 16 == 0 && (d * esz) % 16 == 0;
     if (check_only) return FA_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ELAUNCH;
     BwdArgs a;
     a.q = q;
     a.k = k;
@@ -295,6 +297,7 @@ fa_status run_bwd(const void* q, const void* k, const void* v, const void* o, co
     a.scale_log2 = (float)((double)scale * 1.4426950408889634074);
     a.causal = causal ? 1 : 0;
     a.dtype = (int)dtype;
+    a.num_cus = dev_num_cus(dev);
     const int dpad = (int)((d + 31) / 32) * 32;
     return launch_bwd(a, dpad, vec, stream) == 0 ? FA_OK : FA_ELAUNCH;
 }

@@ -7,9 +7,11 @@
 // That page accumulates dQ with atomic adds from a loop over key tiles; here three kernels
 // share the work without atomics:
 //  * row terms: D = rowsum(dO * O) per query row (fp32, into a caller's workspace);
-//  * dK, dV: one workgroup per 128 keys, looping over query tiles of 64 (4 waves x 32 keys
-//    up to d = 96; above, 8 waves in two roles that split each 32-key block's products);
-//  * dQ: one workgroup per 128 queries (4 waves x 32), looping over key tiles of 64.
+//  * dK, dV: looping over query tiles of 64; up to d = 96 one workgroup per 256 keys (8 waves
+//    x 32 keys) or, on small grids, 128 keys (4 waves); above, one per 128 keys (8 waves in two
+//    roles that split each 32-key block's products);
+//  * dQ: one workgroup per 256 queries (8 waves x 32) or, on small grids, 128 (4 waves),
+//    looping over key tiles of 64.
 // Both tile kernels recompute S and dP on MFMA 32x32x16 (16-bit operands, fp32 accumulate);
 // P and dS are rounded to the input type for the products that consume them.
 //
@@ -35,8 +37,9 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634074f;
-// workgroups an XCD holds at once: 32 CUs x two 4-wave workgroups (two waves per SIMD)
-constexpr int kXcdSlots = 64;
+// workgroups an XCD holds at once (two waves per SIMD): 32 CUs x two 4-wave workgroups, or
+// 32 CUs x one 8-wave workgroup
+constexpr int kXcdSlots = 64, kXcdSlots8 = 32;
 
 // Row terms: delta[r] = sum_c dO[r][c] O[r][c] for every flat query row r (d % 8 == 0, d <= 128).
 // Sixteen lanes share a row, one 16-byte chunk each, so a wave reads four whole rows of O and
@@ -151,13 +154,14 @@ __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* t
 
 // ---------------------------------------------------------------- dK, dV
 
-// dK and dV together for d <= 96, two waves per SIMD: one wave's LDS reads and staged loads
-// then overlap the other's products, about 1.5x the throughput of one wave per SIMD.
-template <typename T, int DP, bool CAUSAL, bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+// dK and dV together for d <= 96, NW waves of 32 keys, two per SIMD: one wave's LDS reads and
+// staged loads then overlap the other's products, about 1.5x the throughput of one wave per
+// SIMD.
+template <typename T, int DP, bool CAUSAL, bool VEC, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     static_assert(DP <= 96, "above d = 96: bwd_dkdv_pair_kernel");
-    constexpr int BK = 128, BQ = 64;  // keys per workgroup, queries per tile
+    constexpr int BK = 32 * NW, BQ = 64;  // keys per workgroup, queries per tile
     constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * STR];
@@ -168,7 +172,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
     // causal: key tile 0 sees every query tile, the heaviest; tile-major dispatch per XCD
-    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, kXcdSlots);
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, NW == 8 ? kXcdSlots8 : kXcdSlots);
     const int bh = pt.pair, kt = pt.tile;
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int k0 = kt * BK;
@@ -198,7 +202,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     // query tiles that see any key of this workgroup (causal: queries >= k0)
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
-    TileCopy<DP, STR, VEC> qc, gc;
+    TileCopy<DP, STR, VEC, 64 * NW> qc, gc;
     qc.init(d, tid);
     gc.init(d, tid);
     float lrow = 0.0f, drow = 0.0f;
@@ -341,7 +345,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
     const int h32 = lane >> 5, l32 = lane & 31;
     const int kbk = wave % KB;
     // one workgroup per CU: an XCD holds 32 at once
-    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, 32);
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_ktiles, a.B * a.H, CAUSAL, kXcdSlots8);
     const int bh = pt.pair, kt = pt.tile;
     const int Nq = a.Nq, Nk = a.Nk, d = a.d;
     const int k0 = kt * BK;
@@ -526,10 +530,10 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
 // ---------------------------------------------------------------- dQ
 
 // Two waves per SIMD at every head dim (the registers fit 256 per wave).
-template <typename T, int DP, bool CAUSAL, bool VEC>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+template <typename T, int DP, bool CAUSAL, bool VEC, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
-    constexpr int BR = 128, BC = 64;  // queries per workgroup, keys per tile
+    constexpr int BR = 32 * NW, BC = 64;  // queries per workgroup, keys per tile
     constexpr int STR = DP + 8;
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * STR];
@@ -537,7 +541,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
-    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL, kXcdSlots);
+    const PairTile pt = xcd_pair_tile(blockIdx.x, gridDim.x, n_qtiles, a.B * a.H, CAUSAL, NW == 8 ? kXcdSlots8 : kXcdSlots);
     const int bh = pt.pair;
     int qt = pt.tile;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first (tile-major dispatch per XCD)
@@ -570,7 +574,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
-    TileCopy<DP, STR, VEC> kc, vc;
+    TileCopy<DP, STR, VEC, 64 * NW> kc, vc;
     kc.init(d, tid);
     vc.init(d, tid);
     kc.load(kg, 0, Nk, d, tid);
@@ -1012,6 +1016,29 @@ int launch_bwd32(const BwdArgs& a, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+// NW-wave launches of the 16-bit dK/dV (d <= 96) and dQ kernels, 32 rows per wave. More waves
+// share each staged tile, so each stages less of it (8 waves measured 2-7% faster than 4 on
+// grids of two or more workgroups per CU); fewer rows per workgroup balance small grids
+// better. The results are the same bit for bit: every wave sums the same tiles in the same order.
+template <typename T, int DP, bool VEC, int NW>
+void launch_dkdv16(const BwdArgs& a, hipStream_t st) {
+    const int n_kt = (a.Nk + 32 * NW - 1) / (32 * NW);
+    const unsigned g = (unsigned)((int64_t)n_kt * a.B * a.H);
+    if (a.causal)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, VEC, NW>), dim3(g), dim3(64 * NW), 0, st, a, n_kt);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, VEC, NW>), dim3(g), dim3(64 * NW), 0, st, a, n_kt);
+}
+template <typename T, int DP, bool VEC, int NW>
+void launch_dq16(const BwdArgs& a, hipStream_t st) {
+    const int n_qt = (a.Nq + 32 * NW - 1) / (32 * NW);
+    const unsigned g = (unsigned)((int64_t)n_qt * a.B * a.H);
+    if (a.causal)
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, true, VEC, NW>), dim3(g), dim3(64 * NW), 0, st, a, n_qt);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, false, VEC, NW>), dim3(g), dim3(64 * NW), 0, st, a, n_qt);
+}
+
 template <typename T, int DP, bool VEC>
 int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)a.B * a.H * a.Nq;
@@ -1025,16 +1052,18 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
                            a.o, a.dout, a.delta, rows, a.d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    const int n_kt = (a.Nk + 127) / 128;
-    const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
+    // dK, dV up to d = 96 and dQ: 8-wave workgroups (256 rows) while their grid still gives
+    // every CU two, else 4-wave ones (128 rows)
+    const bool wide_k = (int64_t)((a.Nk + 255) / 256) * a.B * a.H >= 2 * (int64_t)a.num_cus;
+    const bool wide_q = (int64_t)((a.Nq + 255) / 256) * a.B * a.H >= 2 * (int64_t)a.num_cus;
     if constexpr (DP <= 96) {
-        if (a.causal)
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, true, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
-        else
-            hipLaunchKernelGGL((bwd_dkdv_kernel<T, DP, false, VEC>), dim3(g1), dim3(256), 0, st, a, n_kt);
+        if (wide_k) launch_dkdv16<T, DP, VEC, 8>(a, st);
+        else launch_dkdv16<T, DP, VEC, 4>(a, st);
     } else {
         // above d = 96 the accumulators of both gradients no longer fit one wave at two waves
         // per SIMD: the two-role kernel, 128 keys per workgroup
+        const int n_kt = (a.Nk + 127) / 128;
+        const unsigned g1 = (unsigned)((int64_t)n_kt * a.B * a.H);
         if (a.causal)
             hipLaunchKernelGGL((bwd_dkdv_pair_kernel<T, DP, true, VEC>), dim3(g1), dim3(512), 0, st, a, n_kt);
         else
@@ -1042,12 +1071,8 @@ int launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     }
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
-    const int n_qt = (a.Nq + 127) / 128;
-    const unsigned g2 = (unsigned)((int64_t)n_qt * a.B * a.H);
-    if (a.causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, true, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
-    else
-        hipLaunchKernelGGL((bwd_dq_kernel<T, DP, false, VEC>), dim3(g2), dim3(256), 0, st, a, n_qt);
+    if (wide_q) launch_dq16<T, DP, VEC, 8>(a, st);
+    else launch_dq16<T, DP, VEC, 4>(a, st);
     return (int)hipGetLastError();
 }
 

@@ -71,6 +71,7 @@ struct BwdArgs {
     float scale_log2;  // scale times log2(e)
     int causal;
     int dtype;
+    int num_cus;       // compute units of the device (the workgroup size of two kernels)
 };
 
 // Launches the backward kernels (row terms, dK/dV, dQ) on `stream`; `vec`: every buffer

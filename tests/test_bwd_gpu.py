@@ -138,3 +138,43 @@ def test_bwd_full_size_heads_f32():
     """fp32 at the pages' benchmark shape per head (N=4096, d=64) and at d=128, two heads each."""
     run_case("f32", 1, 4, 4096, 4096, 64, False, seed=7, scale=0.125, heads=[0, 3])
     run_case("f32", 1, 2, 4096, 4096, 128, True, seed=8, heads=[0, 1])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_wide_grids(dt, d, causal):
+    """Grids of two or more 256-row workgroups per CU (4 x 32 heads, 1000 queries, 1100 keys:
+    512 and 640 of them on 256 CUs) take the 8-wave dQ and (d <= 96) dK/dV workgroups, a single
+    head the 4-wave ones. Two heads against the oracle, and every sampled head's gradients
+    equal bit for bit to those of the same head run alone from the same O and L."""
+    B, H, Nq, Nk, seed = 4, 32, 1000, 1100, 400 + d + (1 if causal else 0)
+    scale = 1.0 / math.sqrt(d)
+    q = make_random((B, H, Nq, d), dt, seed)
+    k = make_random((B, H, Nk, d), dt, seed + 1)
+    v = make_random((B, H, Nk, d), dt, seed + 2)
+    do = make_random((B, H, Nq, d), dt, seed + 3)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.attention(qd, kd, vd, scale=scale, causal=causal)
+    dq, dk, dv = fa.attention_bwd(qd, kd, vd, o, lse, dod, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    heads = [0, 77, B * H - 1]
+    flat = lambda t: t.reshape(B * H, *t.shape[2:])
+    for h in heads:
+        one = [flat(t)[h][None, None].contiguous() for t in (qd, kd, vd, o, lse, dod)]
+        g1 = [torch.full_like(t, float("nan")) for t in one[:3]]
+        fa.fa_bwd(*one, *g1, torch.empty_like(one[4]), scale, causal)
+        torch.cuda.synchronize()
+        for name, wide, alone in zip(("dq", "dk", "dv"), (dq, dk, dv), g1):
+            assert torch.equal(flat(wide)[h], alone[0, 0]), (dt, d, causal, h, name)
+    sel = lambda t: t.reshape(B * H, *t.shape[2:])[heads[:2]][None]
+    qs, ks, vs, dos = (torch.from_numpy(sel(t.double().numpy())) for t in (q, k, v, do))
+    want = oracle.attention_bwd(qs, ks, vs, dos, scale, causal, o=sel(o.double().cpu().numpy()))
+    rn = lambda t: float(torch.as_tensor(t).double().norm(dim=-1).max())
+    term = {"dq": scale * rn(dos) * rn(vs) * rn(ks), "dk": scale * rn(dos) * rn(vs) * rn(qs), "dv": rn(dos)}
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        got = sel(got.double().cpu().numpy())
+        mag = max(float(np.max(np.abs(ref))), 1e-3 * term[name])
+        err = float(np.max(np.abs(got - ref)))
+        say(f"  wide {dt} d={d} causal={causal} {name}: normalised {err / mag:.3e}")
+        assert err / mag <= TOL[dt], (dt, d, causal, name, err / mag)
