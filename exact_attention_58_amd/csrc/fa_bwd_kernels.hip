@@ -7,11 +7,11 @@
 // That page accumulates dQ with atomic adds from a loop over key tiles; here three kernels
 // share the work without atomics:
 //  * row terms: D = rowsum(dO * O) per query row (fp32, into a caller's workspace);
-//  * dK, dV: looping over query tiles of 64; up to d = 96 one workgroup per 256 keys (8 waves
-//    x 32 keys) or, on small grids, 128 keys (4 waves); above, one per 128 keys (8 waves in two
-//    roles that split each 32-key block's products);
+//  * dK, dV: looping over query tiles of 128 (d <= 64) or 64; up to d = 96 one workgroup per
+//    256 keys (8 waves x 32 keys) or, on small grids, 128 keys (4 waves); above, one per 128
+//    keys (8 waves in two roles that split each 32-key block's products);
 //  * dQ: one workgroup per 256 queries (8 waves x 32) or, on small grids, 128 (4 waves),
-//    looping over key tiles of 64.
+//    looping over key tiles of 128 (d <= 64, and d <= 96 with 8 waves) or 64.
 // Both tile kernels recompute S and dP on MFMA 32x32x16 (16-bit operands, fp32 accumulate);
 // P and dS are rounded to the input type for the products that consume them.
 //
@@ -93,12 +93,13 @@ void bwd_delta_any_kernel(const void* o, const void* dout, float* delta, int64_t
     if (r < rows && sub == 0) delta[r] = acc;
 }
 
-// Tile of 64 rows x DP columns (16-bit) staged through registers into LDS rows of STR
-// elements; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0, aligned).
-template <int DP, int STR, bool VEC, int NT = 256>
+// Tile of ROWS rows x DP columns (16-bit) staged by NT threads through registers into LDS rows
+// of STR elements; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0,
+// aligned).
+template <int DP, int STR, bool VEC, int NT = 256, int ROWS = 64>
 struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
-    static constexpr int CH = (64 * CPR + NT - 1) / NT;  // chunks per thread (the last maybe partial)
+    static constexpr int CH = (ROWS * CPR + NT - 1) / NT;  // chunks per thread (the last maybe partial)
     u32x4 r[CH];
     // VEC: byte offset of this thread's chunk within a tile, or an offset past any buffer
     // (a chunk past d, or a thread without a chunk) that the load's range check turns into 0
@@ -109,7 +110,7 @@ struct TileCopy {
             for (int c = 0; c < CH; ++c) {
                 const int chunk = tid + c * NT;
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
-                const bool ok = (64 * CPR % NT == 0 || chunk < 64 * CPR) && col < d;
+                const bool ok = (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) && col < d;
                 voff[c] = ok ? (unsigned)(row * d + col) * 2u : kBufferVoid;
             }
         }
@@ -126,7 +127,7 @@ struct TileCopy {
             for (int c = 0; c < CH; ++c) {
                 const int chunk = tid + c * NT;
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
-                if (64 * CPR % NT == 0 || chunk < 64 * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
+                if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
             }
         }
     }
@@ -135,7 +136,7 @@ struct TileCopy {
         for (int c = 0; c < CH; ++c) {
             const int chunk = tid + c * NT;
             const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            if (64 * CPR % NT == 0 || chunk < 64 * CPR) *(u32x4*)(lds + row * STR + col) = r[c];
+            if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) *(u32x4*)(lds + row * STR + col) = r[c];
         }
     }
 };
@@ -161,7 +162,8 @@ template <typename T, int DP, bool CAUSAL, bool VEC, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     static_assert(DP <= 96, "above d = 96: bwd_dkdv_pair_kernel");
-    constexpr int BK = 32 * NW, BQ = 64;  // keys per workgroup, queries per tile
+    // keys per workgroup, queries per tile (128 where the registers allow: half the barriers)
+    constexpr int BK = 32 * NW, BQ = DP <= 64 ? 128 : 64;
     constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * STR];
@@ -202,7 +204,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     // query tiles that see any key of this workgroup (causal: queries >= k0)
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
-    TileCopy<DP, STR, VEC, 64 * NW> qc, gc;
+    TileCopy<DP, STR, VEC, 64 * NW, BQ> qc, gc;
     qc.init(d, tid);
     gc.init(d, tid);
     float lrow = 0.0f, drow = 0.0f;
@@ -231,7 +233,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
         if (CAUSAL && q0 + BQ - 1 < kw0) continue;
 
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < BQ / 32; ++qb) {
             // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
             f32x16 s = f32x16{}, dp = f32x16{};
             const uint16_t* qp = Qs + (qb * 32 + l32) * STR + 8 * h32;
@@ -533,7 +535,8 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
 template <typename T, int DP, bool CAUSAL, bool VEC, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
-    constexpr int BR = 32 * NW, BC = 64;  // queries per workgroup, keys per tile
+    // queries per workgroup, keys per tile (128 where the registers allow: half the barriers)
+    constexpr int BR = 32 * NW, BC = DP <= 64 || (DP <= 96 && NW == 8) ? 128 : 64;
     constexpr int STR = DP + 8;
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * STR];
@@ -574,7 +577,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
-    TileCopy<DP, STR, VEC, 64 * NW> kc, vc;
+    TileCopy<DP, STR, VEC, 64 * NW, BC> kc, vc;
     kc.init(d, tid);
     vc.init(d, tid);
     kc.load(kg, 0, Nk, d, tid);
@@ -591,11 +594,11 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
         const int k0 = j * BC;
         if (CAUSAL && k0 > r0w + 31) continue;
 
-        // S^T = K Q^T and dP^T = V dO^T: two 32-key blocks; register r of block kb is key
+        // S^T = K Q^T and dP^T = V dO^T: BC/32 blocks of 32 keys; register r of block kb is key
         // k0 + kb*32 + 8 (r/4) + 4 h32 + r%4, query myq
-        unsigned pk[2][8];
+        unsigned pk[BC / 32][8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < BC / 32; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
             const uint16_t* kp = Ks + (kb * 32 + l32) * STR + 8 * h32;
             const uint16_t* vp = Vs + (kb * 32 + l32) * STR + 8 * h32;
@@ -623,7 +626,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
             if ((DP <= 96 || !CAUSAL) && VEC && full) weights(std::false_type{});
             else weights(std::true_type{});
         }
-        // dQ^T += K^T dS^T: four 16-key steps
+        // dQ^T += K^T dS^T: BC/16 steps of 16 keys
 #pragma unroll
         for (int t = 0; t < BC / 16; ++t) {
             const u32x4 sb = {pk[t >> 1][4 * (t & 1) + 0], pk[t >> 1][4 * (t & 1) + 1],
