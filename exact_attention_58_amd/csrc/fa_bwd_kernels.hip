@@ -622,8 +622,9 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) pk[kb][r >> 1] = Half<T>::pack2(sv[r], sv[r + 1]);
             };
-            // (the unmasked copy not for causal d = 128, where it does not fit the registers)
-            if ((DP <= 96 || !CAUSAL) && VEC && full) weights(std::false_type{});
+            // (the unmasked copy not for causal d = 128 at 4 waves, where it does not fit the
+            // registers; 8 waves stage half as many chunks per thread)
+            if ((DP <= 96 || !CAUSAL || NW == 8) && VEC && full) weights(std::false_type{});
             else weights(std::true_type{});
         }
         // dQ^T += K^T dS^T: BC/16 steps of 16 keys
