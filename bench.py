@@ -146,7 +146,7 @@ def time_workload(fa, torch, w, steps, warmup, inputs=None, keep_outputs=False):
 def time_backward(fa, torch, w, steps, warmup):
     """Times fa_bwd (row terms, dK/dV, dQ kernels) on the workload's inputs and a seeded
     upstream gradient, after one forward for O and L; returns ms per call (HIP events on
-    the launch stream)."""
+    the launch stream) and the number of untimed warm-up calls before the timed ones."""
     from exact_attention_58_amd.workloads import make_inputs, make_random
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in make_inputs(w))
@@ -155,8 +155,8 @@ def time_backward(fa, torch, w, steps, warmup):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    warm_up(torch, lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.softmax_scale, w.causal, stream),
-            warmup, stream)
+    n_warm = warm_up(torch, lambda: fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.softmax_scale,
+                                              w.causal, stream), warmup, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -166,7 +166,7 @@ def time_backward(fa, torch, w, steps, warmup):
     torch.cuda.synchronize(dev)
     ms = e0.elapsed_time(e1) / steps
     del q, k, v, do, o, lse, dq, dk, dv, delta
-    return ms
+    return ms, n_warm
 
 
 def time_varlen(fa, torch, causal, steps, warmup):
@@ -353,6 +353,9 @@ def main():
                          "e.g. 4,16,4096,4096,32,bf16,0")
     ap.add_argument("--quick", action="store_true", help="headline only: no other workloads, sweep or CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--backward", action="store_true",
+                    help="only time fa_bwd on the workload (warm-up calls, then the timed calls; "
+                         "prints one JSON line): the command the backward profiles run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -391,6 +394,16 @@ def main():
         w = Workload(f"shape_{B_}x{H_}x{Nq_}x{Nk_}x{d_}_{dt_}{'_causal' if int(c_) else ''}", int(B_), int(H_),
                      int(Nq_), int(Nk_), int(d_), dt_, bool(int(c_)), seed=11)
         args.quick = True
+    if args.backward:
+        ms, n_warm = time_backward(fa, torch, w, args.steps, args.warmup)
+        tf = 2.5 * w.flops / (ms * 1e-3) / 1e12
+        log(f"  {w.name} backward: calls {n_warm}..{n_warm + args.steps - 1} of fa_bwd are the timed region "
+            f"({n_warm} warm-up calls before them), {ms:.4f} ms per call, {tf:.1f} TFLOP/s")
+        print(json.dumps({"metric": "attention bwd TFLOP/s (FLOP = 2.5 x the forward's)", "workload": w.name,
+                          "value": round(tf, 2), "unit": "TFLOP/s", "ms_per_call": round(ms, 4),
+                          "steps": args.steps, "warmup": args.warmup, "dtype": w.dtype,
+                          "pct_of_peak": round(100 * tf / PEAK_TFLOPS[w.dtype], 2)}), flush=True)
+        return
     with_oracle = not args.quick and not args.no_cpu
     log(f"headline {w.name}: {args.warmup} warmup + {args.steps} timed steps")
     torch.cuda.synchronize()
@@ -424,7 +437,7 @@ def main():
         # size; this implementation recomputes S and dP in both tile kernels)
         for name in ("d128_bf16", "d128_bf16_causal", "long_causal_bf16", "pages_f32"):
             ow = WORKLOADS[name]
-            ms = time_backward(fa, torch, ow, max(5, min(args.steps, 20)), 2)
+            ms, _ = time_backward(fa, torch, ow, max(5, min(args.steps, 20)), 2)
             tf = 2.5 * ow.flops / (ms * 1e-3) / 1e12
             peak = PEAK_TFLOPS[ow.dtype]
             also.append({"workload": f"{name} backward", "B": ow.B, "H": ow.H, "Nq": ow.Nq, "Nk": ow.Nk,
