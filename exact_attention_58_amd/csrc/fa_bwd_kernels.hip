@@ -93,10 +93,54 @@ void bwd_delta_any_kernel(const void* o, const void* dout, float* delta, int64_t
     if (r < rows && sub == 0) delta[r] = acc;
 }
 
-// Tile of ROWS rows x DP columns (16-bit) staged by NT threads through registers into LDS rows
-// of STR elements; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0,
+// LDS layout of the 16-bit tiles (Q, dO, K, V: rows x DP). Swizzled (d = 32, 64, 128): rows of
+// P 16-byte chunks, P = 4 or 12 (mod 16), and chunk c of row r at position c ^ ((r >> 2) & 3)
+// of its row (the low two bits of the chunk index permuted by the row's next two bits). On 64
+// banks of 4 bytes this serves both reads of a tile without conflicts: a b128 read of one
+// chunk from 16 consecutive rows (16 lanes at a time: row pitch and permutation spread them
+// over the 16 bank groups) and a transposed b64 read of 4 consecutive chunks from 4 rows (32
+// lanes at a time: the pitch puts the 4 rows in 4 distinct groups of 4 chunks). The plain
+// pitch of CPR + 1 chunks serves only the first and costs the second 2-4x its cycles; d = 96
+// keeps it, since the swizzle's two extra address registers make its kernels spill.
+template <int DP>
+struct Tile16 {
+    static constexpr bool SWZ = DP != 96;
+    static constexpr int CPR = DP / 8;                                     // chunks of data per row
+    static constexpr int P = !SWZ ? CPR + 1 : CPR % 8 == 0 ? CPR + 4 : CPR;  // chunks per LDS row
+    static constexpr int STR = 8 * P;                                      // elements per LDS row
+    static_assert(!SWZ || P % 8 == 4, "row pitch of 4 or 12 chunks mod 16");
+    // element offset of chunk c of row r
+    __device__ static int off(int r, int c) {
+        return r * STR + 8 * (SWZ ? (c & ~3) | ((c & 3) ^ ((r >> 2) & 3)) : c);
+    }
+};
+
+// Row-major operand reads of a Tile16 tile: lane (h32, l32) reads chunk 2 ds + h32 of row
+// R + l32 (R % 16 == 0). Swizzled, with z = h32 ^ ((l32 >> 2) & 3), that chunk sits at
+// position 4 (ds >> 1) + (z or z ^ 2 by the parity of ds): two offsets per lane, the rest
+// constant.
+template <int DP>
+struct RowFrag {
+    int o0, o1;
+    __device__ explicit RowFrag(int lane) {
+        const int h32 = lane >> 5, l32 = lane & 31;
+        if constexpr (Tile16<DP>::SWZ) {
+            o0 = l32 * Tile16<DP>::STR + 8 * (h32 ^ ((l32 >> 2) & 3));
+            o1 = o0 ^ 16;  // l32 * STR is a multiple of 32 elements
+        } else {
+            o0 = l32 * Tile16<DP>::STR + 8 * h32;
+            o1 = o0 + 16;
+        }
+    }
+    __device__ __attribute__((always_inline)) u32x4 operator()(const uint16_t* tile, int R, int ds) const {
+        return *(const u32x4*)(tile + (ds & 1 ? o1 : o0) + R * Tile16<DP>::STR + 32 * (ds >> 1));
+    }
+};
+
+// Tile of ROWS rows x DP columns (16-bit) staged by NT threads through registers into LDS in
+// the Tile16 layout; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0,
 // aligned).
-template <int DP, int STR, bool VEC, int NT = 256, int ROWS = 64>
+template <int DP, bool VEC, int NT = 256, int ROWS = 64>
 struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
     static constexpr int CH = (ROWS * CPR + NT - 1) / NT;  // chunks per thread (the last maybe partial)
@@ -135,21 +179,27 @@ struct TileCopy {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int chunk = tid + c * NT;
-            const int row = chunk / CPR, col = (chunk % CPR) * 8;
-            if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) *(u32x4*)(lds + row * STR + col) = r[c];
+            const int row = chunk / CPR;
+            if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) *(u32x4*)(lds + Tile16<DP>::off(row, chunk % CPR)) = r[c];
         }
     }
 };
 
-// Transposed fragment of a 64-row LDS tile (rows = reduction index): lane gets rows
+// Transposed fragment of a Tile16 tile (rows = reduction index): lane gets rows
 // R + 4 h32 + {0..3} and R + 8 + 4 h32 + {0..3} of column C + 16 g16 + i16, the B (or A)
-// operand of a 32x32x16 product whose reduction runs over 16 rows in accumulator order.
-template <int STR>
+// operand of a 32x32x16 product whose reduction runs over 16 rows in accumulator order
+// (R % 16 == 0, C % 32 == 0). Each lane reads 4 elements of chunk C/8 + y, y = 2 g16 +
+// (i16 & 3) / 2, whose position in the first row group is y ^ h32 ((row >> 2) & 3 = h32) and
+// in the second y ^ h32 ^ 2.
+template <int DP>
 __device__ __attribute__((always_inline)) inline u32x4 tr_frag(const uint16_t* tile, int R, int C, int lane) {
+    constexpr int STR = Tile16<DP>::STR;
     const int h32 = lane >> 5, i16 = lane & 15, g16 = (lane >> 4) & 1;
-    const uint16_t* p = tile + (R + 4 * h32 + (i16 >> 2)) * STR + C + 16 * g16 + 4 * (i16 & 3);
-    const u32x2 lo = lds_read_tr16(p);
-    const u32x2 hi = lds_read_tr16(p + 8 * STR);
+    const int row = R + 4 * h32 + (i16 >> 2);
+    const int y = 2 * g16 + ((i16 & 3) >> 1), e = 4 * (i16 & 1);
+    const int k = Tile16<DP>::SWZ ? h32 : 0;
+    const u32x2 lo = lds_read_tr16(tile + row * STR + C + 8 * (y ^ k) + e);
+    const u32x2 hi = lds_read_tr16(tile + (row + 8) * STR + C + 8 * (Tile16<DP>::SWZ ? y ^ k ^ 2 : y) + e);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -164,7 +214,7 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     static_assert(DP <= 96, "above d = 96: bwd_dkdv_pair_kernel");
     // keys per workgroup, queries per tile (128 where the registers allow: half the barriers)
     constexpr int BK = 32 * NW, BQ = DP <= 64 ? 128 : 64;
-    constexpr int STR = DP + 8;       // LDS row stride (elements): 16-byte pad
+    constexpr int STR = Tile16<DP>::STR;
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Qs[BQ * STR];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[BQ * STR];  // dO
@@ -204,9 +254,10 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
     // query tiles that see any key of this workgroup (causal: queries >= k0)
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int n_qt = (Nq + BQ - 1) / BQ;
-    TileCopy<DP, STR, VEC, 64 * NW, BQ> qc, gc;
+    TileCopy<DP, VEC, 64 * NW, BQ> qc, gc;
     qc.init(d, tid);
     gc.init(d, tid);
+    const RowFrag<DP> rf(lane);
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int qt) __attribute__((always_inline)) {
         qc.load(qg, qt * BQ, Nq, d, tid);
@@ -236,12 +287,10 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
         for (int qb = 0; qb < BQ / 32; ++qb) {
             // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
             f32x16 s = f32x16{}, dp = f32x16{};
-            const uint16_t* qp = Qs + (qb * 32 + l32) * STR + 8 * h32;
-            const uint16_t* gp = Gs + (qb * 32 + l32) * STR + 8 * h32;
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
-                s = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], s);
-                dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+                s = Half<T>::mfma(rf(Qs, qb * 32, ds), kf[ds], s);
+                dp = Half<T>::mfma(rf(Gs, qb * 32, ds), vf[ds], dp);
             }
             // register r: query q0 + qb*32 + 8 (r/4) + 4 h32 + r%4, key mykey. The weight is
             // kept iff off = 8 (r/4) + r%4 >= lo: lo puts the causal diagonal (q >= mykey) in
@@ -286,9 +335,9 @@ void bwd_dkdv_kernel(BwdArgs a, int n_ktiles) {
                 const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const u32x4 gb = tr_frag<STR>(Gs, qb * 32 + 16 * t, db * 32, lane);
+                    const u32x4 gb = tr_frag<DP>(Gs, qb * 32 + 16 * t, db * 32, lane);
                     dva[db] = Half<T>::mfma(pa, gb, dva[db]);
-                    const u32x4 qbf = tr_frag<STR>(Qs, qb * 32 + 16 * t, db * 32, lane);
+                    const u32x4 qbf = tr_frag<DP>(Qs, qb * 32 + 16 * t, db * 32, lane);
                     dka[db] = Half<T>::mfma(sa, qbf, dka[db]);
                 }
             }
@@ -332,7 +381,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
     constexpr int KB = 4;  // key blocks of 32 per workgroup (one per SIMD)
     constexpr int NT = 128 * KB;
     constexpr int BK = 32 * KB, BQ = 64;
-    constexpr int STR = DP + 8;
+    constexpr int STR = Tile16<DP>::STR;
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Qsb[2][BQ * STR];
     __shared__ __attribute__((aligned(16))) uint16_t Gsb[2][BQ * STR];  // dO
@@ -366,9 +415,10 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
     const int qt0 = CAUSAL ? k0 / BQ : 0;
     const int nt = max((Nq + BQ - 1) / BQ - qt0, 0);
     const int n_steps = nt > 0 ? 2 * nt + 1 : 0;
-    TileCopy<DP, STR, VEC, NT> qc, gc;
+    TileCopy<DP, VEC, NT> qc, gc;
     qc.init(d, tid);
     gc.init(d, tid);
+    const RowFrag<DP> rf(lane);
     float lrow = 0.0f, drow = 0.0f;
     auto load_tile = [&](int t) __attribute__((always_inline)) {
         const int r0 = (qt0 + t) * BQ;
@@ -447,10 +497,9 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
             if (s < 2 * nt && step_active(s)) {
                 const int b = (s >> 1) & 1, qb = s & 1;
                 const int qbase = (qt0 + (s >> 1)) * BQ + qb * 32;
-                const uint16_t* qp = Qsb[b] + (qb * 32 + l32) * STR + 8 * h32;
                 f32x16 sacc = f32x16{};
 #pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) sacc = Half<T>::mfma(*(const u32x4*)(qp + ds * 16), kf[ds], sacc);
+                for (int ds = 0; ds < NDS; ++ds) sacc = Half<T>::mfma(rf(Qsb[b], qb * 32, ds), kf[ds], sacc);
                 // register r: query qbase + 8 (r/4) + 4 h32 + r%4, key mykey; kept iff
                 // 8 (r/4) + r%4 >= lo (key past Nk: none; causal: on or below the diagonal).
                 // Padded query rows need no test: their Q, dO and L are zero, and their weight
@@ -481,7 +530,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
                     const u32x4 pa = {ppk[4 * t], ppk[4 * t + 1], ppk[4 * t + 2], ppk[4 * t + 3]};
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        dva[db] = Half<T>::mfma(pa, tr_frag<STR>(Gsb[b], qb * 32 + 16 * t, db * 32, lane), dva[db]);
+                        dva[db] = Half<T>::mfma(pa, tr_frag<DP>(Gsb[b], qb * 32 + 16 * t, db * 32, lane), dva[db]);
                 }
             }
             end_step();
@@ -500,10 +549,9 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
             const int i = s - 1;
             if (i >= 0 && step_active(i)) {
                 const int b = (i >> 1) & 1, qb = i & 1;
-                const uint16_t* gp = Gsb[b] + (qb * 32 + l32) * STR + 8 * h32;
                 f32x16 dp = f32x16{};
 #pragma unroll
-                for (int ds = 0; ds < NDS; ++ds) dp = Half<T>::mfma(*(const u32x4*)(gp + ds * 16), vf[ds], dp);
+                for (int ds = 0; ds < NDS; ++ds) dp = Half<T>::mfma(rf(Gsb[b], qb * 32, ds), vf[ds], dp);
                 unsigned spk[8];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -520,7 +568,7 @@ void bwd_dkdv_pair_kernel(BwdArgs a, int n_ktiles) {
                     const u32x4 sa = {spk[4 * t], spk[4 * t + 1], spk[4 * t + 2], spk[4 * t + 3]};
 #pragma unroll
                     for (int db = 0; db < NDB; ++db)
-                        dka[db] = Half<T>::mfma(sa, tr_frag<STR>(Qsb[b], qb * 32 + 16 * t, db * 32, lane), dka[db]);
+                        dka[db] = Half<T>::mfma(sa, tr_frag<DP>(Qsb[b], qb * 32 + 16 * t, db * 32, lane), dka[db]);
                 }
             }
             end_step();
@@ -537,7 +585,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_
 void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
     // queries per workgroup, keys per tile (128 where the registers allow: half the barriers)
     constexpr int BR = 32 * NW, BC = DP <= 64 || (DP <= 96 && NW == 8) ? 128 : 64;
-    constexpr int STR = DP + 8;
+    constexpr int STR = Tile16<DP>::STR;
     constexpr int NDS = DP / 16, NDB = DP / 32;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[BC * STR];
@@ -577,9 +625,10 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
     for (int i = 0; i < NDB; ++i) dqa[i] = f32x16{};
 
-    TileCopy<DP, STR, VEC, 64 * NW, BC> kc, vc;
+    TileCopy<DP, VEC, 64 * NW, BC> kc, vc;
     kc.init(d, tid);
     vc.init(d, tid);
+    const RowFrag<DP> rf(lane);
     kc.load(kg, 0, Nk, d, tid);
     vc.load(vg, 0, Nk, d, tid);
     for (int j = 0; j < n_tiles; ++j) {
@@ -600,12 +649,10 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
-            const uint16_t* kp = Ks + (kb * 32 + l32) * STR + 8 * h32;
-            const uint16_t* vp = Vs + (kb * 32 + l32) * STR + 8 * h32;
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
-                s = Half<T>::mfma(*(const u32x4*)(kp + ds * 16), qf[ds], s);
-                dp = Half<T>::mfma(*(const u32x4*)(vp + ds * 16), gf[ds], dp);
+                s = Half<T>::mfma(rf(Ks, kb * 32, ds), qf[ds], s);
+                dp = Half<T>::mfma(rf(Vs, kb * 32, ds), gf[ds], dp);
             }
             const int lim = (CAUSAL ? min(Nk - 1, myq) : Nk - 1) - k0 - kb * 32 - 4 * h32;
             // every key of the block below Nk and (causal) at or before every query of the wave
@@ -634,7 +681,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
                               pk[t >> 1][4 * (t & 1) + 2], pk[t >> 1][4 * (t & 1) + 3]};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const u32x4 ka = tr_frag<STR>(Ks, 16 * t, db * 32, lane);
+                const u32x4 ka = tr_frag<DP>(Ks, 16 * t, db * 32, lane);
                 dqa[db] = Half<T>::mfma(ka, sb, dqa[db]);
             }
         }
