@@ -236,10 +236,13 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 // softmax's vector work dominates). Without the key split, head dims up to 32, and up to 64
 // when not causal, compile for three waves per SIMD (at most 168 registers; non-causal d = 64:
 // 16-19% faster on short sequences, 7-8% on small grids); the causal d = 64 instances keep the
-// budget of two, whose grids of two workgroups per CU at a time measured ahead.
+// budget of two, whose grids of two workgroups per CU at a time measured ahead. The key split
+// at d = 64 takes three as well (causal B1 H16 N4096: 62 -> 54 us; at d = 32 it would spill).
 template <int DP, int SPLIT, bool CAUSAL>
 constexpr int fwd16_waves_per_simd() {
-    return DP > 128 ? 1 : (SPLIT == 1 && (DP <= 32 || (DP <= 64 && !CAUSAL))) ? 3 : 2;
+    return DP > 128 ? 1
+           : ((SPLIT == 1 && (DP <= 32 || (DP <= 64 && !CAUSAL))) || (SPLIT == 2 && DP == 64)) ? 3
+                                                                                             : 2;
 }
 
 template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
