@@ -235,19 +235,23 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 // Head dims up to 32 run 128-key tiles (half the barriers and reductions per key, where the
 // softmax's vector work dominates). Without the key split, head dims up to 32, and up to 64
 // when not causal, compile for three waves per SIMD (at most 168 registers; non-causal d = 64:
-// 16-19% faster on short sequences, 7-8% on small grids); the causal d = 64 instances keep the
-// budget of two, whose grids of two workgroups per CU at a time measured ahead. The key split
-// at d = 64 takes three as well (causal B1 H16 N4096: 62 -> 54 us; at d = 32 it would spill).
-template <int DP, int SPLIT, bool CAUSAL>
+// 16-19% faster on short sequences, 7-8% on small grids), and so does non-causal d = 96 over
+// 16-byte rows (B16 H64 N512: 156 -> 138 us; its element-wise instance would spill); the
+// causal d = 64 instances keep the budget of two, whose grids of two workgroups per CU at a
+// time measured ahead. The key split at d = 64 takes three as well (causal B1 H16 N4096:
+// 62 -> 54 us; at d = 32 it would spill).
+template <int DP, int SPLIT, bool CAUSAL, bool VEC>
 constexpr int fwd16_waves_per_simd() {
     return DP > 128 ? 1
-           : ((SPLIT == 1 && (DP <= 32 || (DP <= 64 && !CAUSAL))) || (SPLIT == 2 && DP == 64)) ? 3
-                                                                                             : 2;
+           : ((SPLIT == 1 && (DP <= 32 || (DP <= 64 && !CAUSAL) || (DP == 96 && !CAUSAL && VEC))) ||
+              (SPLIT == 2 && DP == 64))
+               ? 3
+               : 2;
 }
 
 template <typename T, int DP, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(fwd16_waves_per_simd<DP, SPLIT, CAUSAL>(), fwd16_waves_per_simd<DP, SPLIT, CAUSAL>())))
+                          amdgpu_waves_per_eu(fwd16_waves_per_simd<DP, SPLIT, CAUSAL, VEC>(), fwd16_waves_per_simd<DP, SPLIT, CAUSAL, VEC>())))
 void fwd16_kernel(FwdArgs a, int n_qtiles) {
     // Causal grids split too: a workgroup's rows start at q0 = 64 t and its key tiles end at
     // its diagonal, so the second half starts at key 64 ceil((t + 1) / 2) <= q0 and every row
@@ -283,7 +287,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
     const int rbk = wave % RB, half = wave / RB;  // row block, key half
 
     // an XCD holds 32 CUs x (workgroups per CU) of these at once
-    const TileId wt = tile_of(a, n_qtiles, 32 * fwd16_waves_per_simd<DP, SPLIT, CAUSAL>());
+    const TileId wt = tile_of(a, n_qtiles, 32 * fwd16_waves_per_simd<DP, SPLIT, CAUSAL, VEC>());
     const int bh = wt.bh;
     int qt = wt.qt;
     if (CAUSAL) qt = n_qtiles - 1 - qt;  // longest rows first
