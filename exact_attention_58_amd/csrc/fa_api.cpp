@@ -172,11 +172,11 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // 575 vs 515 TFLOP/s).
         const int64_t wgs256 = (Nq + 255) / 256 * B * H;
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
-        // non-causal d <= 64 on grids of three or more 128-row workgroups per CU: the 4-wave
-        // kernel (three waves per SIMD there) up to 1536 keys (B32 H16 N768: 128 -> 100 us,
-        // B16 H16 N1024: 105 -> 90, B4 H16 N1536: 70 -> 56; B2 H16 N1536, 1.5 per CU: 34 vs 38
-        // for the ping-pong kernel)
-        const int64_t pp_min_keys = !causal ? (c.dpad <= 64 && wgs128 >= 3 * (int64_t)num_cus ? 1536 : 512)
+        // non-causal d <= 96 on grids of three or more 128-row workgroups per CU: the 4-wave
+        // kernel (three waves per SIMD there) up to 1536 keys (d64: B32 H16 N768 128 -> 100 us,
+        // B16 H16 N1024 105 -> 90, B4 H16 N1536 70 -> 56; d96: B32 H16 N768 177 -> 156, B4 H16
+        // N1536 94 -> 74; B2 H16 N1536 d64, 1.5 per CU: 34 vs 38 for the ping-pong kernel)
+        const int64_t pp_min_keys = !causal ? (c.dpad <= 96 && wgs128 >= 3 * (int64_t)num_cus ? 1536 : 512)
                                             : d <= 64 ? 2560 : 2048;
         const bool causal_split = causal && wgs128 <= 2 * (int64_t)num_cus;
         if (d > 128) {

@@ -253,13 +253,14 @@ def test_select_config_grid_fill(dtype):
     assert edge["waves"] == 4
     longer = fa.fa_select_config(dtype, 8, 128, 1024, 513, 128, False, num_cus=256)
     assert longer["waves"] == 8
-    # non-causal d <= 64 with three or more 128-row workgroups per CU: the 4-wave kernel up
-    # to 1536 keys; fewer per CU, or more keys: the ping-pong kernel
+    # non-causal d <= 96 with three or more 128-row workgroups per CU: the 4-wave kernel up
+    # to 1536 keys; fewer per CU, more keys or d = 128: the ping-pong kernel
     assert fa.fa_select_config(dtype, 4, 16, 1536, 1536, 64, False, num_cus=256)["waves"] == 4
     assert fa.fa_select_config(dtype, 16, 16, 1024, 1024, 48, False, num_cus=256)["waves"] == 4
     assert fa.fa_select_config(dtype, 2, 16, 1536, 1536, 64, False, num_cus=256)["waves"] == 8
     assert fa.fa_select_config(dtype, 4, 16, 2048, 1537, 64, False, num_cus=256)["waves"] == 8
-    assert fa.fa_select_config(dtype, 16, 16, 1024, 1024, 96, False, num_cus=256)["waves"] == 8
+    assert fa.fa_select_config(dtype, 16, 16, 1024, 1024, 96, False, num_cus=256)["waves"] == 4
+    assert fa.fa_select_config(dtype, 16, 16, 1024, 1024, 128, False, num_cus=256)["waves"] == 8
     assert fa.fa_select_config(dtype, 16, 16, 1024, 1024, 64, True, num_cus=256)["waves"] == 4
     # head dims up to 32: the 4-wave kernel at every length
     for causal in (False, True):
