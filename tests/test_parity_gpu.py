@@ -168,6 +168,21 @@ def test_tuned_rule_shapes(dt, B, H, N, d, causal, waves, br):
     full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} B{B} H{H} N{N} d{d} causal={causal}")
 
 
+@pytest.mark.parametrize("dt,B,H,N,d,causal,br", [
+    ("bf16", 16, 16, 1024, 64, False, 128),  # non-causal d <= 96, 3+ per CU, <= 1536 keys: 4-wave
+    ("f16", 4, 16, 1536, 96, False, 128),    # the same at d = 96 (three waves per SIMD)
+    ("bf16", 8, 16, 1000, 48, False, 128),   # d = 48 (padded to 64), ragged rows
+    ("f16", 1, 16, 4096, 64, True, 64),      # the causal d = 64 key split (three waves per SIMD)
+])
+def test_four_wave_short_key_shapes(dt, B, H, N, d, causal, br):
+    """Grids where the 4-wave kernel, compiled for three waves per SIMD, is chosen over the
+    ping-pong kernel: every row against the oracle."""
+    cfg = fa.fa_select_config(dt, B, H, N, N, d, causal)
+    assert (cfg["waves"], cfg["Br"]) == (4, br), cfg
+    q, k, v = (make_random((B, H, N, d), dt, 970 + i) for i in range(3))
+    full_check(q, k, v, 1.0 / math.sqrt(d), causal, dt, f"{dt} B{B} H{H} N{N} d{d} causal={causal}")
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_increasing_scores_force_rescales(dt):
     """Scores that grow along the keys: every tile raises the row max by more than the
