@@ -179,6 +179,7 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         const int64_t pp_min_keys = !causal ? (c.dpad <= 96 && wgs128 >= 3 * (int64_t)num_cus ? 1536 : 512)
                                             : d <= 64 ? 2560 : 2048;
         const bool causal_split = causal && wgs128 <= 2 * (int64_t)num_cus;
+        const bool split_nc = !causal && (wgs128 <= (int64_t)num_cus || (c.dpad <= 64 && 2 * wgs128 <= 3 * (int64_t)num_cus));
         if (d > 128) {
             // head dims past 128: the 4-wave kernel, one wave per SIMD
         } else if (aligned && d % 8 == 0 && d > 32 && wgs256 * 8 >= (int64_t)num_cus * (causal ? 8 : 5) &&
@@ -188,14 +189,16 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
             c.waves = 8;
             c.br = 256;
             c.bc = pp_keys(c.dpad);
-        } else if (c.dpad <= 128 && (wgs128 < num_cus || causal_split) && Nk > 2 * c.bc) {
+        } else if (c.dpad <= 128 && (split_nc || causal_split) && Nk > 2 * c.bc) {
             // too few 128-row workgroups to fill the chip: 64 rows per workgroup, each row
             // block's keys walked in two halves by two waves and merged at the end. Causal
             // grids split up to two workgroups per CU: their uneven workgroups leave a tail
             // that the split halves (B1 H20 N2048 d64 causal: 46.1 -> 33.2 us; at two per CU,
             // B1 H16 N4096 d64: 77 -> 64 us, B1 H32 N2048 d64: 42 -> 38 us). Non-causal
-            // grids between one and two per CU measured slower split (B1 H56 N1024 d128:
-            // 45.4 vs 59.9 us).
+            // grids split up to one per CU (B1 H8 N4096 d64: 62 -> 51 us, d96: 77 -> 70, d128:
+            // 111 -> 101), and up to 1.5 per CU for d <= 64 (B1 H9 N4096 d64: 87 -> 71-73 us,
+            // B1 H12 N4096 d32: 64-67 -> 62-64), not above (B1 H9 N4096 d96: 113-118 vs
+            // 116-119 us; B1 H56 N1024 d128, 1.75 per CU: 45.4 vs 59.9 us).
             c.br = 64;
         }
     }

@@ -295,8 +295,8 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    least three 128-row workgroups per CU; causal: more than 2048, or 2560 for d <= 64),
  *    except causal grids with d <= 96 and at most two 128-row workgroups per
  *    CU; otherwise the 4-wave kernel (128 rows; 128-key tiles up to d = 32, 32-key tiles
- *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of fewer 128-row
- *    workgroups than CUs (at most two per CU for causal grids).
+ *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of at most one
+ *    128-row workgroup per CU (1.5 for d <= 64; two for causal grids).
  *  - fp32: one 4-wave kernel per head dim (128 rows; 128-key tiles up to d = 64, 64-key
  *    tiles up to d = 96, 32-key tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
  *    (four per CU for causal grids).

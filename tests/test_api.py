@@ -225,11 +225,19 @@ def test_select_config_grid_fill(dtype):
     assert small["waves"] == 4 and small["Br"] == 64
     small_causal = fa.fa_select_config(dtype, 2, 12, 1000, 3001, 96, True, num_cus=256)
     assert small_causal["waves"] == 4 and small_causal["Br"] == 64  # causal grids split too
-    # between one and two 128-row workgroups per CU: causal grids split, non-causal do not
+    # between one and two 128-row workgroups per CU: causal grids split
     assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["Br"] == 64
-    # non-causal: the ping-pong kernel down to 5/8 of a 256-row workgroup per CU
+    # non-causal: the ping-pong kernel down to 5/8 of a 256-row workgroup per CU; below it the
+    # key split up to one 128-row workgroup per CU (1.5 for d <= 64), the 4-wave kernel above
     assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, False, num_cus=256)["Br"] == 256
-    assert fa.fa_select_config(dtype, 1, 16, 2048, 2048, 64, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config(dtype, 1, 16, 2048, 2048, 64, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 8, 4096, 4096, 96, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 9, 4096, 4096, 96, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config(dtype, 1, 9, 4096, 4096, 64, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 12, 4096, 4096, 32, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 13, 4096, 4096, 32, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config(dtype, 1, 8, 4096, 4096, 128, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config(dtype, 1, 9, 4096, 4096, 128, False, num_cus=256)["Br"] == 128
     assert fa.fa_select_config(dtype, 1, 20, 2048, 2048, 64, True, num_cus=256)["waves"] == 4
     assert fa.fa_select_config(dtype, 1, 40, 2048, 2048, 64, True, num_cus=256)["Br"] == 128
     # causal grids of exactly two 128-row workgroups per CU: the key split up to d = 96, the
