@@ -123,7 +123,7 @@ def test_large_magnitude_scores(dt):
         full_check(q, k, v, 0.125, causal, dt, f"{dt} large scores causal={causal}")
 
 
-@pytest.mark.parametrize("B,H,Nq,waves_br", [(1, 1, 4, (4, 64)), (4, 64, 128, (4, 128))])
+@pytest.mark.parametrize("B,H,Nq,waves_br", [(1, 1, 4, (4, 64)), (4, 128, 128, (4, 128))])
 def test_fp16_denormal_weights(B, H, Nq, waves_br):
     """Weights in the fp16 denormal range: one key has weight 1 and the 3000 others weight
     2^-16 in every row, so together they raise l by 4.6% and L by 0.045. The PV product
