@@ -135,9 +135,11 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // fewer 128-row workgroups than the chip holds (two per CU): the key split, also for
         // causal grids (measured below 2 per CU: B1 H20 N2048 d64 265 -> 221 us, causal
         // B1 H40 N1024 97 -> 74 us). d <= 96: at d = 128 the split's two staged tiles no
-        // longer fit the registers.
+        // longer fit the registers. At d = 96 the split runs one wave per SIMD, and
+        // non-causal grids split only below one per CU (B2 H16 N1024: 128 -> 109 us unsplit).
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
-        if (c.dpad <= 96 && wgs128 < (causal ? 4 : 2) * num_cus && Nk > 2 * c.bc) c.br = 64;
+        const int64_t split_below = causal ? 4 : c.dpad > 64 ? 1 : 2;
+        if (c.dpad <= 96 && wgs128 < split_below * num_cus && Nk > 2 * c.bc) c.br = 64;
         // Causal grids (tuned on MI355X): the split up to four workgroups per CU, in dispatch
         // groups of 128 (B1 H16 N4096 d64: 402 -> 294 us; B1 H64 N1024: 107 -> 91 us; B1 H40
         // N1024 d64 split 71.6 -> 63.2 us with groups of 128), and above d = 96, for grids of

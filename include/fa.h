@@ -299,7 +299,7 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    128-row workgroup per CU (1.5 for d <= 64; two for causal grids).
  *  - fp32: one 4-wave kernel per head dim (128 rows; 128-key tiles up to d = 64, 64-key
  *    tiles up to d = 96, 32-key tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
- *    (four per CU for causal grids).
+ *    (one per CU for non-causal d > 64, four per CU for causal grids).
  * The scheduling knobs of fa_fwd_config that the built-in rules set (dispatch groups of 128
  * for the causal fp32 key split, and one workgroup per CU for causal fp32 grids above d = 96
  * with at most two 128-row workgroups per CU) are not reported; they change no result bit.

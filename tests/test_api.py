@@ -297,6 +297,10 @@ def test_select_config_fp32_key_split():
     assert fa.fa_select_config("f32", 1, 16, 4096, 4096, 64, True, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 1, 64, 4096, 4096, 64, True, num_cus=256)["Br"] == 128
     assert fa.fa_select_config("f32", 1, 8, 1024, 128, 64, False, num_cus=256)["Br"] == 128
+    # non-causal d = 96 splits only below one per CU (the split runs one wave per SIMD there)
+    assert fa.fa_select_config("f32", 1, 8, 2048, 2048, 96, False, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 2, 16, 1024, 1024, 96, False, num_cus=256)["Br"] == 128
+    assert fa.fa_select_config("f32", 2, 16, 1024, 1024, 96, True, num_cus=256)["Br"] == 64
 
 
 def test_select_config_errors():
