@@ -82,7 +82,8 @@ struct TileId {
     int bh, qt;
 };
 // slots: the workgroups one group of pairs should hold at least. The 4-wave kernels pass what
-// an XCD holds at once (32 CUs x 2); the ping-pong kernel passes twice its 32 resident ones,
+// an XCD holds at once (32 CUs x 2 or 3, their waves per SIMD); the ping-pong kernel passes
+// twice its 32 resident ones,
 // which measured about 2% faster on dense causal grids of 2 or more pairs per XCD (packed
 // batches: 32).
 __device__ __attribute__((always_inline)) inline TileId tile_of(const FwdArgs& a, int n_qtiles, int slots) {
