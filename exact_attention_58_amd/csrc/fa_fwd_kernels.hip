@@ -234,17 +234,16 @@ __device__ __attribute__((always_inline)) inline float pack_and_sum(const f32x16
 // half merges them: m = max(m1, m2), l = l1 2^(m1-m) + l2 2^(m2-m), O likewise, the same
 // exact combination the online recurrence makes tile by tile.
 // Head dims up to 32 run 128-key tiles (half the barriers and reductions per key, where the
-// softmax's vector work dominates). Without the key split, head dims up to 32, and up to 64
-// when not causal, compile for three waves per SIMD (at most 168 registers; non-causal d = 64:
-// 16-19% faster on short sequences, 7-8% on small grids), and so does non-causal d = 96 over
-// 16-byte rows (B16 H64 N512: 156 -> 138 us; its element-wise instance would spill); the
-// causal d = 64 instances keep the budget of two, whose grids of two workgroups per CU at a
-// time measured ahead. The key split at d = 64 takes three as well (causal B1 H16 N4096:
-// 62 -> 54 us; at d = 32 it would spill).
+// softmax's vector work dominates). Without the key split, head dims up to 64 compile for
+// three waves per SIMD (at most 168 registers; non-causal d = 64: 16-19% faster on short
+// sequences, 7-8% on small grids; causal B4 H32 N2048 d64: 106 -> 91 us), and so does
+// non-causal d = 96 over 16-byte rows (B16 H64 N512: 156 -> 138 us; its element-wise instance
+// would spill). The key split at d = 64 takes three as well (causal B1 H16 N4096: 62 -> 54 us;
+// at d = 32 it would spill).
 template <int DP, int SPLIT, bool CAUSAL, bool VEC>
 constexpr int fwd16_waves_per_simd() {
     return DP > 128 ? 1
-           : ((SPLIT == 1 && (DP <= 32 || (DP <= 64 && !CAUSAL) || (DP == 96 && !CAUSAL && VEC))) ||
+           : ((SPLIT == 1 && (DP <= 64 || (DP == 96 && !CAUSAL && VEC))) ||
               (SPLIT == 2 && DP == 64))
                ? 3
                : 2;
