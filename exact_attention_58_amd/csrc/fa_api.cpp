@@ -178,8 +178,13 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         // kernel (three waves per SIMD there) up to 1536 keys (d64: B32 H16 N768 128 -> 100 us,
         // B16 H16 N1024 105 -> 90, B4 H16 N1536 70 -> 56; d96: B32 H16 N768 177 -> 156, B4 H16
         // N1536 94 -> 74; B2 H16 N1536 d64, 1.5 per CU: 34 vs 38 for the ping-pong kernel)
+        // causal d <= 64 on grids of eight or more 128-row workgroups per CU: the 4-wave kernel
+        // (three waves per SIMD) up to 4096 keys (B4 H32 N3072: 233 -> 214 us, B4 H16 N4096
+        // d48: 187 -> 175; B4 H32 N4096 367 vs 370; at 3-4 per CU the ping-pong kernel stays
+        // ahead: B2 H16 N3072 65 vs 69, B1 H8 N16384 331 vs 364)
         const int64_t pp_min_keys = !causal ? (c.dpad <= 96 && wgs128 >= 3 * (int64_t)num_cus ? 1536 : 512)
-                                            : d <= 64 ? 2560 : 2048;
+                                  : d <= 64 ? (wgs128 >= 8 * (int64_t)num_cus ? 4096 : 2560)
+                                            : 2048;
         const bool causal_split = causal && wgs128 <= 2 * (int64_t)num_cus;
         const bool split_nc = !causal && (wgs128 <= (int64_t)num_cus || (c.dpad <= 64 && 2 * wgs128 <= 3 * (int64_t)num_cus));
         if (d > 128) {

@@ -292,7 +292,8 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    d = 64, 64-key tiles above) for aligned rows with d % 8 == 0 and 32 < d <= 128, when
  *    its grid has at least 5/8 of a workgroup per CU (one per CU for causal grids) and the
  *    key length passes the crossover (more than 512 keys, or 1536 for d <= 96 on grids of at
- *    least three 128-row workgroups per CU; causal: more than 2048, or 2560 for d <= 64),
+ *    least three 128-row workgroups per CU; causal: more than 2048, or for d <= 64 more than
+ *    2560, 4096 on grids of at least eight 128-row workgroups per CU),
  *    except causal grids with d <= 96 and at most two 128-row workgroups per
  *    CU; otherwise the 4-wave kernel (128 rows; 128-key tiles up to d = 32, 32-key tiles
  *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of at most one

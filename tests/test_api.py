@@ -273,12 +273,13 @@ def test_select_config_grid_fill(dtype):
     # head dims up to 32: the 4-wave kernel at every length
     for causal in (False, True):
         assert fa.fa_select_config(dtype, 4, 16, 16384, 16384, 32, causal, num_cus=256)["waves"] == 4
-    # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 2560 keys (d <= 64)
-    for d, last_4wave in ((128, 2048), (96, 2048), (64, 2560)):
-        at = fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, True, num_cus=256)
-        past = fa.fa_select_config(dtype, 4, 32, last_4wave + 1, last_4wave + 1, d, True, num_cus=256)
+    # causal grids keep the 4-wave kernel up to 2048 keys (d > 64) or 2560 keys (d <= 64;
+    # 4096 on grids of eight or more 128-row workgroups per CU)
+    for B, d, last_4wave in ((4, 128, 2048), (4, 96, 2048), (2, 64, 2560), (4, 64, 4096)):
+        at = fa.fa_select_config(dtype, B, 32, last_4wave, last_4wave, d, True, num_cus=256)
+        past = fa.fa_select_config(dtype, B, 32, last_4wave + 1, last_4wave + 1, d, True, num_cus=256)
         assert at["waves"] == 4 and past["waves"] == 8, (d, at, past)
-        assert fa.fa_select_config(dtype, 4, 32, last_4wave, last_4wave, d, False, num_cus=256)["waves"] == 8
+        assert fa.fa_select_config(dtype, B, 32, last_4wave, last_4wave, d, False, num_cus=256)["waves"] == 8
 
 
 def test_select_config_fp32_key_split():
