@@ -102,9 +102,9 @@ def test_varlen_pingpong_kernel(causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_varlen_pingpong_kernel_128_key_tiles(causal):
     """d = 64: the ping-pong kernel's 128-key tiles over packed sequences, most of them ending
-    in a partial tile. The longest sequence passes 2560 keys, where causal grids at d <= 64
-    leave the 4-wave kernel."""
-    lq = [2700, 700, 513, 1, 999, 256, 0, 130]
+    in a partial tile. The longest sequence passes 4096 keys, where causal grids at d <= 64
+    leave the 4-wave kernel at any grid size."""
+    lq = [4200, 700, 513, 1, 999, 256, 0, 130]
     run_case("bf16", 16, lq, lq, 64, causal, seed=53, heads=[0, 15], expect_waves=8)
 
 
