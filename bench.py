@@ -37,17 +37,17 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67566255, "kernel_sha": "f0feb42736bf84a3"},
+    "pages_f32": {"bytes": 67566255, "kernel_sha": "8d37d85592638a65"},
     # profiles/fwd32_tiny_causal_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "tiny_causal_f32": {"bytes": 543190, "kernel_sha": "f0feb42736bf84a3"},
+    "tiny_causal_f32": {"bytes": 543190, "kernel_sha": "8d37d85592638a65"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269680367, "kernel_sha": "f0feb42736bf84a3"},
+    "d128_bf16": {"bytes": 269680367, "kernel_sha": "8d37d85592638a65"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 355439162, "kernel_sha": "f0feb42736bf84a3"},
+    "d128_bf16_causal": {"bytes": 356240738, "kernel_sha": "8d37d85592638a65"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78349076, "kernel_sha": "f0feb42736bf84a3"},
+    "long_causal_bf16": {"bytes": 78357549, "kernel_sha": "8d37d85592638a65"},
     # profiles/fwd16_split_ragged_f16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "ragged_f16": {"bytes": 37117028, "kernel_sha": "f0feb42736bf84a3"},
+    "ragged_f16": {"bytes": 37116900, "kernel_sha": "8d37d85592638a65"},
 }
 
 
