@@ -488,15 +488,56 @@ constexpr int tree_slot(int r) {
     return 0;
 }
 
-// LDS row pitches. The LDS serves 256 bytes per clock over 64 four-byte banks, i.e. 16 bank
-// groups of 16 bytes; a b128 read is served 16 lanes at a time and a 64-bit transposed read 32
-// lanes at a time. K fragments read 16 consecutive rows at one 16-byte chunk: an odd pitch (in
-// chunks) puts them in 16 distinct groups. V^T fragments read 4 consecutive rows x 4 aligned
-// chunks: a pitch of 4 or 12 chunks mod 16 puts them in 16 distinct groups. Padding rather
-// than an XOR swizzle keeps every operand address a per-lane base plus an immediate offset.
-template <int DP> struct Pitch {
-    static constexpr int K = DP / 8 + 1;                                         // chunks
-    static constexpr int V = (DP == 128 || DP == 64) ? DP / 8 + 4 : DP / 8;      // chunks
+// LDS layouts of the K and V tiles. The LDS serves 256 bytes per clock over 64 four-byte
+// banks, i.e. 16 bank groups of 16 bytes; a b128 read is served 16 lanes at a time and a
+// 64-bit transposed read 32 lanes at a time. A K fragment read takes one 16-byte chunk from
+// each of 16 consecutive key rows, a V^T fragment read 4 aligned chunks from each of 4
+// consecutive key rows: each must fall in 16 distinct bank groups, and every operand address
+// stays a per-lane base plus an immediate offset. A tile is filled by 1 KB copy instructions
+// (lane i writes 16-byte slot i), so the layout is chosen by where each slot loads from.
+//  * Dense (rows of 4, 8 or 16 chunks): no padding slots, so a copy moves only data. A
+//    256-byte K line holds chunks 2m and 2m+1 of 8 consecutive rows, chunk c of row r in slot
+//    2(r&7) + ((c ^ (r >> 3)) & 1): the 16 rows of a read lie in two lines, one per slot
+//    parity. A V line holds 4 aligned chunks of 4 consecutive rows, which is exactly what one
+//    half-wave of a transposed read takes. One copy instruction covers whole rows or whole
+//    128-byte row segments.
+//  * Padded (d = 96): K rows of 13 chunks (odd, so 16 consecutive rows spread over the 16
+//    groups) and V rows of 12 (12 mod 16 spreads 4 rows x 4 chunks). Here the dense lines
+//    would cut the 192-byte rows into pieces of 32 and 64 bytes.
+template <int DP> struct KvLayout {
+    static constexpr int CPR = DP / 8;  // 16-byte data chunks per row
+    static constexpr bool DENSE = (CPR & (CPR - 1)) == 0;
+    static constexpr int KP = DENSE ? CPR : CPR + 1, VP = CPR;  // slots per row
+    // key row r and chunk c that slot p of a K (isk) or V tile holds
+    __device__ static void slot_rc(bool isk, int p, int& r, int& c) {
+        const int line = p >> 4, q = p & 15;
+        if (!DENSE) {
+            const int pitch = isk ? KP : VP;
+            r = p / pitch;
+            c = p - r * pitch;
+        } else if (isk) {
+            r = 8 * (line / (CPR / 2)) + (q >> 1);
+            c = 2 * (line % (CPR / 2)) + ((q ^ (r >> 3)) & 1);
+        } else {
+            r = 4 * (line / (CPR / 4)) + (q >> 2);
+            c = 4 * (line % (CPR / 4)) + (q & 3);
+        }
+    }
+    // K fragment of key rows 32kb + l32, chunk 2ds + h32: per-lane base + koff(kb, ds)
+    __device__ static unsigned kbase(int l32, int h32) {
+        return DENSE ? (l32 >> 3) * (CPR / 2) * 256 + 32 * (l32 & 7) + 16 * ((h32 ^ (l32 >> 3)) & 1)
+                     : l32 * KP * 16 + h32 * 16;
+    }
+    static constexpr int koff(int kb, int ds) { return DENSE ? kb * CPR * 512 + ds * 256 : kb * 32 * KP * 16 + ds * 32; }
+    // V^T fragment: lane (i16, g16, h32) reads key row 16t + 8hi + 4h32 + i16/4, bytes
+    // 64db + 32g16 + 8(i16 & 3) of it: per-lane base + voff(t, db, hi)
+    __device__ static unsigned vbase(int h32, int i16, int g16) {
+        return DENSE ? h32 * (CPR / 4) * 256 + (i16 >> 2) * 64 + 32 * g16 + 8 * (i16 & 3)
+                     : (4 * h32 + (i16 >> 2)) * VP * 16 + (16 * g16 + 4 * (i16 & 3)) * 2;
+    }
+    static constexpr int voff(int t, int db, int hi) {
+        return DENSE ? (4 * t + 2 * hi) * (CPR / 4) * 256 + db * 256 : (16 * t + 8 * hi) * VP * 16 + db * 64;
+    }
 };
 
 // 16-bit forward kernel for aligned inputs with d % 8 == 0: 8 waves in two groups of four.
@@ -524,16 +565,15 @@ template <int DP> struct Pitch {
 // neither costs time.
 // Key tiles hold 64 keys, and 128 up to DP = 64: there a 64-key phase is short (16 MFMAs),
 // and the longer tile halves the barriers, row-max reductions and rescale tests per key
-// (about 7% faster at d = 64; three K and four V buffers of 128 keys take 150 KB of LDS).
+// (about 7% faster at d = 64; three K and four V buffers of 128 keys take 112 KB of LDS).
 template <typename T, int DP, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     constexpr int WPG = 4, NWAVE = 2 * WPG;
     constexpr int BR = 32 * NWAVE, BC = pp_keys(DP);
     constexpr int NKB = BC / 32;
-    constexpr int DCH = DP / 8;                    // 16-byte data chunks per row
-    constexpr int KP = Pitch<DP>::K, VP = Pitch<DP>::V;
-    constexpr int KTILEB = BC * KP * 16, VTILEB = BC * VP * 16;
+    using L = KvLayout<DP>;
+    constexpr int KTILEB = BC * L::KP * 16, VTILEB = BC * L::VP * 16;
     constexpr int NDS = DP / 16;
     constexpr int NDB = DP / 32;
 
@@ -574,24 +614,23 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     const int n = (kv_end + BC - 1) / BC;
     const int dchunks = d / 8;
 
-    // Direct HBM->LDS copy of the K and V tiles into rows of KP / VP chunks. The copy of a
-    // tile pair is KI + VI wave instructions (64 lanes x 16 B, wave-uniform LDS destination,
-    // lane i -> +16*i); instruction c = it*NWAVE + wave belongs to this wave. A lane on a
-    // padding chunk loads a valid chunk of its row into the padding, which is never read, so
-    // the copy of a full tile needs no lane mask. Chunks past d (DP > d) repeat the row's last
+    // Direct HBM->LDS copy of the K and V tiles in the KvLayout. The copy of a tile pair is
+    // KI + VI wave instructions (64 lanes x 16 B, wave-uniform LDS destination, lane i ->
+    // +16*i); instruction c = it*NWAVE + wave belongs to this wave. A lane on a padding slot
+    // loads a valid chunk of its row into the padding, which is never read, so the copy of a
+    // full tile needs no lane mask. Chunks past d (DP > d) repeat the row's last
     // data chunk: finite, and Q is zero there, so they add nothing to the scores. A tile that
     // runs past Nk repeats row Nk-1 in its tail rows (finite; their scores are masked and
     // their weights are zero); only that last tile takes the slower clamped path.
-    constexpr int KI = KP * BC / 64, VI = VP * BC / 64;  // copy instructions per K / V tile
+    constexpr int KI = L::KP * BC / 64, VI = L::VP * BC / 64;  // copy instructions per K / V tile
     constexpr int NCP = (KI + VI + NWAVE - 1) / NWAVE;
     unsigned coff[NCP];  // lane's byte offset within a full tile (row r, column chunk)
 #pragma unroll
     for (int it = 0; it < NCP; ++it) {
         const int c = it * NWAVE + wave;
-        const int pitch = c < KI ? KP : VP;
         const int idx = c < KI ? c : c - KI;
-        const int p = idx * 64 + lane;
-        const int r = p / pitch, cch = p - r * pitch;
+        int r, cch;
+        L::slot_rc(c < KI, idx * 64 + lane, r, cch);
         coff[it] = (unsigned)(r * d + min(cch, dchunks - 1) * 8) * 2u;
     }
     auto kbuf = [&](int j) __attribute__((always_inline)) { return smem + (j % NKBUF) * KTILEB; };
@@ -607,9 +646,8 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
         if (m * BC + BC <= Nk) {
             __builtin_amdgcn_global_load_lds((const void*)(tile + coff[it]), (FA_LDS void*)dst, 16, 0, 0);
         } else {
-            const int pitch = isk ? KP : VP;
-            const int p = idx * 64 + lane;
-            const int r = p / pitch, cch = p - r * pitch;
+            int r, cch;
+            L::slot_rc(isk, idx * 64 + lane, r, cch);
             const int rr = min(r, Nk - 1 - m * BC);
             const unsigned off = (unsigned)(rr * d + min(cch, dchunks - 1) * 8) * 2u;
             __builtin_amdgcn_global_load_lds((const void*)(tile + off), (FA_LDS void*)dst, 16, 0, 0);
@@ -641,8 +679,8 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
     constexpr int LA = 6;
     const int i16 = lane & 15, g16 = (lane >> 4) & 1;
     // per-lane operand bases (LDS byte addresses); every fragment is base + compile-time offset
-    const unsigned kbase = l32 * KP * 16 + h32 * 16;
-    const unsigned vbase = (4 * h32 + (i16 >> 2)) * VP * 16 + (16 * g16 + 4 * (i16 & 3)) * 2;
+    const unsigned kbase = L::kbase(l32, h32);
+    const unsigned vbase = L::vbase(h32, i16, g16);
     const unsigned smem_a = lds_addr(smem);
     auto kaddr = [&](int j) __attribute__((always_inline)) { return smem_a + (j % NKBUF) * KTILEB + kbase; };
     auto vaddr = [&](int j) __attribute__((always_inline)) { return smem_a + NKBUF * KTILEB + (j % NVBUF) * VTILEB + vbase; };
@@ -650,13 +688,12 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
         constexpr int i = decltype(ic)::value;
         if constexpr (i < NP) {
             constexpr int t = i / NDB, db = i % NDB;
-            constexpr int off = t * 16 * VP * 16 + db * 64;
-            const u32x2 lo = lds_rdtr16<off>(va);
-            const u32x2 hi = lds_rdtr16<off + 8 * VP * 16>(va);
+            const u32x2 lo = lds_rdtr16<L::voff(t, db, 0)>(va);
+            const u32x2 hi = lds_rdtr16<L::voff(t, db, 1)>(va);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
             constexpr int qi = i - NP, ds = qi / NKB, kb = qi % NKB;
-            return lds_rd128<kb * 32 * KP * 16 + ds * 32>(ka);
+            return lds_rd128<L::koff(kb, ds)>(ka);
         }
     };
     u32x4 ring[LA];
