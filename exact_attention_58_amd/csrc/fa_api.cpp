@@ -55,8 +55,8 @@ fa_status check_args(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t N
 // Whether `cfg` names a kernel that exists for these inputs: the 16-bit kernels are the
 // ping-pong kernel (8 waves, 256 rows: 16-byte rows, d % 8 == 0, d <= 128), the 4-wave kernel
 // (128 rows) and its key-split form (64 rows: d <= 128); fp32 has one kernel per head dim
-// and its key-split form (64 rows: d <= 96). The tile keys and the padded head dim are fixed
-// by dtype and d.
+// and its key-split forms (64 rows in two parts, 32 rows in four: d <= 96). The tile keys
+// and the padded head dim are fixed by dtype and d.
 bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool aligned) {
     const int dpad = (int)((d + 31) / 32) * 32;
     if (cfg.dpad != dpad) return false;
@@ -64,7 +64,7 @@ bool config_ok(const TileConfig& cfg, int dtype, int64_t d, int causal, bool ali
     if (cfg.group != 0 && (cfg.group < 8 || cfg.group > 1024)) return false;
     if (dtype == FA_F32)
         return cfg.waves == 4 && cfg.bc == f32_keys(dpad, cfg.br, aligned) &&
-               (cfg.br == 128 || (cfg.br == 64 && dpad <= 96));
+               (cfg.br == 128 || ((cfg.br == 64 || cfg.br == 32) && dpad <= 96));
     if (cfg.waves == 8) return cfg.bc == pp_keys(dpad) && cfg.br == 256 && aligned && d % 8 == 0 && dpad <= 128;
     if (cfg.bc != (dpad > 224 ? 32 : dpad <= 32 ? 128 : 64)) return false;
     if (cfg.waves != 4) return false;
@@ -140,6 +140,15 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         const int64_t wgs128 = (Nq + 127) / 128 * B * H;
         const int64_t split_below = causal ? 4 : c.dpad > 64 ? 1 : 2;
         if (c.dpad <= 96 && wgs128 < split_below * num_cus && Nk > 2 * c.bc) c.br = 64;
+        // smaller grids still: 32 rows per workgroup, the keys in four parts, up to one such
+        // workgroup per CU (four for causal grids; half a one for d = 96, where the split
+        // runs one wave per SIMD). Measured against the two-way split (fp32, us): B1 H1 N256
+        // d64 causal 12.9 -> 9.4; B1 H2 N4096 d64 155 -> 96; B1 H16 N2048 d64 causal 106 ->
+        // 92; B2 H4 N512 d96 causal 34 -> 23; past the limits it loses (B1 H16 N2048 d64 133
+        // -> 154, B1 H16 N4096 d64 causal 290 -> 326, B1 H8 N2048 d96 122 -> 148).
+        const int64_t wgs32 = (Nq + 31) / 32 * B * H;
+        const int64_t four_below = c.dpad > 64 ? num_cus / 2 : causal ? 4 * (int64_t)num_cus : num_cus;
+        if (c.br == 64 && wgs32 <= four_below) c.br = 32;
         // Causal grids (tuned on MI355X): the split up to four workgroups per CU, in dispatch
         // groups of 128 (B1 H16 N4096 d64: 402 -> 294 us; B1 H64 N1024: 107 -> 91 us; B1 H40
         // N1024 d64 split 71.6 -> 63.2 us with groups of 128), and above d = 96, for grids of
@@ -416,8 +425,9 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     const int bc16 = dpad > 224 ? 32 : dpad <= 32 ? 128 : 64;
     const int bc128 = dtype == FA_F32 ? fa::f32_keys(dpad, 128, aligned) : bc16;
     const int bc64 = dtype == FA_F32 ? fa::f32_keys(dpad, 64, aligned) : bc16;
-    constexpr int kCand = 3;
-    const fa::TileConfig cand[kCand] = {{256, fa::pp_keys(dpad), 8, dpad, 0, 0}, {128, bc128, 4, dpad, 0, 0}, {64, bc64, 4, dpad, 0, 0}};
+    constexpr int kCand = 4;
+    const fa::TileConfig cand[kCand] = {{256, fa::pp_keys(dpad), 8, dpad, 0, 0}, {128, bc128, 4, dpad, 0, 0},
+                                        {64, bc64, 4, dpad, 0, 0}, {32, fa::f32_keys(dpad, 32, aligned), 4, dpad, 0, 0}};
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return FA_ELAUNCH;
@@ -427,7 +437,7 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
     }
     fa_status result = FA_EUNSUPPORTED;
     // one untimed launch each; it also rejects configurations with no kernel for these inputs
-    bool admitted[kCand] = {false, false, false};
+    bool admitted[kCand] = {};
     for (int i = 0; i < kCand && result != FA_ELAUNCH; ++i) {
         st = fa::run_fwd(q, k, v, o, lse, nullptr, nullptr, B, H, Nq, Nk, 0, 0, d, scale, causal, dtype,
                          stream, &cand[i]);
@@ -461,7 +471,7 @@ fa_status fa_tune_fwd(const void* q, const void* k, const void* v, void* o, floa
         if (ms < 0.0f) result = FA_ELAUNCH;
         warm_ms += ms;
     }
-    float best_round[kCand] = {0.0f, 0.0f, 0.0f};
+    float best_round[kCand] = {};
     for (int round = 0; round < 2 && result == FA_OK; ++round)
         for (int i = 0; i < kCand && result == FA_OK; ++i) {
             if (!admitted[i]) continue;

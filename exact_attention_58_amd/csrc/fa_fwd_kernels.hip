@@ -844,14 +844,18 @@ void fwd16_pp_kernel(FwdArgs a, int n_qtiles) {
 // and of K. P stays fp32 for the PV product. SPLIT = 2 (grids too small to fill the chip)
 // works as in the 16-bit kernel: 64 rows per workgroup, the two waves of a row block each
 // walk one half of the key tiles (one LDS tile buffer per half) and the halves' (O, m, l)
-// merge through LDS at the end. Causal grids may split too: a workgroup's rows start at
-// q0 = 64 t and its tiles end at its diagonal, so the second half starts at key
-// 64 ceil((t + 1) / 2) <= q0 and every row sees a key of the first tile it processes (for
-// t = 0 the second half has no tile and merges as zero weight).
+// merge through LDS at the end. SPLIT = 4 (still smaller grids) gives a workgroup one row
+// block of 32 rows whose four waves each walk a quarter of the key tiles (32-key tiles, so
+// the four staged tiles fit the registers), merged the same way in quarter order: on the
+// fp32 matrix core a wave's chain of products is what a small grid waits for, and the
+// quarters cut it by half again. Causal grids may split too: every tile a workgroup
+// processes starts at or before its first row q0 (its tiles end at its diagonal, and the
+// last one starts at most at q0), so every row sees a key of the first tile of each part;
+// a part with no tile (small t) merges as zero weight.
 template <int DP, int BC, bool CAUSAL, bool VEC, int SPLIT>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void fwd32_kernel(FwdArgs a, int n_qtiles) {
-    static_assert(SPLIT == 1 || SPLIT == 2, "one or two key halves");
+    static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "one, two or four key parts");
     constexpr int NW = 4, RB = NW / SPLIT, BR = 32 * RB;
     constexpr int KST = DP + 4;  // floats; 16-byte pad
     constexpr int VST = DP;      // floats
@@ -869,7 +873,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     constexpr int NBUF = SPLIT;
     __shared__ __attribute__((aligned(16))) float Ks[NBUF][BC * KST];
     __shared__ __attribute__((aligned(16))) float Vs[NBUF][BC * VST];
-    static_assert(SPLIT == 1 || RB * (NDB * 16 + 2) * 64 <= NBUF * BC * KST, "merge fits the K buffers");
+    static_assert(SPLIT == 1 || (SPLIT - 1) * RB * (NDB * 16 + 2) * 64 <= NBUF * BC * KST, "merge fits the K buffers");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h32 = lane >> 5, l32 = lane & 31;
@@ -998,46 +1002,62 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
                 }
         }
     };
-    if constexpr (SPLIT == 2) {
-        // step i stages tile h * n_steps + i of each half h into buffer h
-        const int n_steps = (n_tiles + 1) / 2;
-        load_tile_h(0, 0);
-        load_tile_h(1, n_steps);
+    if constexpr (SPLIT > 1) {
+        // step i stages tile h * n_steps + i of each part h into buffer h
+        const int n_steps = (n_tiles + SPLIT - 1) / SPLIT;
+#pragma unroll
+        for (int h = 0; h < SPLIT; ++h) load_tile_h(h, h * n_steps);
         for (int i = 0; i < n_steps; ++i) {
             __syncthreads();
-            store_tile_h(0, 0);
-            store_tile_h(1, 1);
+#pragma unroll
+            for (int h = 0; h < SPLIT; ++h) store_tile_h(h, h);
             __syncthreads();
             if (i + 1 < n_steps) {
-                load_tile_h(0, i + 1);
-                load_tile_h(1, n_steps + i + 1);
+#pragma unroll
+                for (int h = 0; h < SPLIT; ++h) load_tile_h(h, h * n_steps + i + 1);
             }
             const int j = half * n_steps + i;
-            if (j < n_tiles) tile(j, Ks[half], Vs[half]);  // the second half may have one tile less
+            if (j < n_tiles) tile(j, Ks[half], Vs[half]);  // a later part may have fewer tiles
         }
-        // merge the key halves: half 1 hands (O, m, l) to half 0 through LDS (lane-contiguous
-        // rows of 64 floats)
+        // merge the key parts: parts 1.. hand (O, m, l) to part 0 through LDS (lane-contiguous
+        // rows of 64 floats); part 0 adds them in part order
         constexpr int NV = NDB * 16 + 2;
-        float* mrg = &Ks[0][0] + rbk * NV * 64;
+        auto mrg = [&](int h) __attribute__((always_inline)) { return &Ks[0][0] + ((h - 1) * RB + rbk) * NV * 64; };
         __syncthreads();  // every wave is done with the tile buffers
-        if (half == 1) {
+        if (half > 0) {
+            float* w = mrg(half);
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mrg[(db * 16 + r) * 64 + lane] = oacc[db][r];
-            mrg[(NV - 2) * 64 + lane] = m_run;
-            mrg[(NV - 1) * 64 + lane] = l_run;
+                for (int r = 0; r < 16; ++r) w[(db * 16 + r) * 64 + lane] = oacc[db][r];
+            w[(NV - 2) * 64 + lane] = m_run;
+            w[(NV - 1) * 64 + lane] = l_run;
         }
         __syncthreads();
-        if (half == 1) return;
-        const float m2 = mrg[(NV - 2) * 64 + lane], l2 = mrg[(NV - 1) * 64 + lane];
-        const float m = fmaxf(m_run, m2);  // finite: half 0 has seen key tile 0
-        const float a1 = __builtin_amdgcn_exp2f(m_run - m), a2 = __builtin_amdgcn_exp2f(m2 - m);
+        if (half > 0) return;
+        float m = m_run;  // finite: part 0 has seen key tile 0
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int h = 1; h < SPLIT; ++h) m = fmaxf(m, mrg(h)[(NV - 2) * 64 + lane]);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - m);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a1 + mrg[(db * 16 + r) * 64 + lane] * a2;
-        l_run = l_run * a1 + l2 * a2;
+        for (int h = 1; h < SPLIT; ++h) {
+            const float* w = mrg(h);
+            const float ah = __builtin_amdgcn_exp2f(w[(NV - 2) * 64 + lane] - m);
+            const float lh = w[(NV - 1) * 64 + lane];
+            if (h == 1) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + w[(db * 16 + r) * 64 + lane] * ah;
+                l_run = l_run * a0 + lh * ah;
+            } else {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] += w[(db * 16 + r) * 64 + lane] * ah;
+                l_run += lh * ah;
+            }
+        }
         m_run = m;
     } else {
         load_tile(0);
@@ -1148,7 +1168,14 @@ static int launch16(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream
 template <int DP, int BC>
 static int launch32(const FwdArgs& a, const TileConfig& cfg, bool vec, hipStream_t st) {
     if constexpr (DP <= 96) {
-        if (cfg.br == 64) {  // key split (d <= 96: checked by the caller)
+        if (cfg.br == 32) {  // key split in four, 32-key tiles (d <= 96: checked by the caller)
+            if (a.causal)
+                return vec ? launch(fwd32_kernel<DP, 32, true, true, 4>, a, 32, st, 256, cfg.occ)
+                           : launch(fwd32_kernel<DP, 32, true, false, 4>, a, 32, st, 256, cfg.occ);
+            return vec ? launch(fwd32_kernel<DP, 32, false, true, 4>, a, 32, st, 256, cfg.occ)
+                       : launch(fwd32_kernel<DP, 32, false, false, 4>, a, 32, st, 256, cfg.occ);
+        }
+        if (cfg.br == 64) {  // key split in two (d <= 96: checked by the caller)
             if (a.causal)
                 return vec ? launch(fwd32_kernel<DP, BC, true, true, 2>, a, 64, st, 256, cfg.occ)
                            : launch(fwd32_kernel<DP, BC, true, false, 2>, a, 64, st, 256, cfg.occ);

@@ -41,9 +41,10 @@ struct TileConfig {
 // Keys per K/V tile of the 16-bit ping-pong kernel for a padded head dim.
 constexpr int pp_keys(int dpad) { return dpad <= 64 ? 128 : 64; }
 // Keys per K/V tile of the fp32 kernel: 128 up to d = 64 for 128-row workgroups over
-// 16-byte rows, 32 above d = 96, else 64 (the key split and element-wise rows keep 64).
+// 16-byte rows, 32 above d = 96 and for the four-way key split (32-row workgroups), else 64
+// (the two-way key split and element-wise rows keep 64).
 constexpr int f32_keys(int dpad, int br, bool aligned) {
-    return dpad > 96 ? 32 : (dpad <= 64 && br == 128 && aligned) ? 128 : 64;
+    return dpad > 96 || br == 32 ? 32 : (dpad <= 64 && br == 128 && aligned) ? 128 : 64;
 }
 
 // Pure selection logic (no HIP calls). Returns 0 on success, 2 if no kernel fits.

@@ -141,8 +141,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  * (128, Bc, 4) and its two-way key split (64, Bc, 4, d <= 128), with Bc = 128 keys for
  * d <= 32, 32 for d > 224 and 64 otherwise. For fp32, (128, 128, 4) for d <= 64 when every
  * buffer is 16-byte aligned and d % 4 == 0, otherwise (128, 64, 4) for d <= 96; (128, 32, 4)
- * above d = 96; and (64, 64, 4) when d <= 96. Any other triple returns FA_EUNSUPPORTED
- * before any HIP call.
+ * above d = 96; and the key splits (64, 64, 4) and (32, 32, 4) when d <= 96. Any other
+ * triple returns FA_EUNSUPPORTED before any HIP call.
  * Two knobs change only where and when workgroups run, never a result bit:
  *  - occ (0..4): at most occ workgroups on one CU at a time, by reserving unused LDS
  *    (160 KB / occ per workgroup); 0 = as many as the registers and LDS allow.
@@ -299,8 +299,11 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    above d = 224), or its two-way key split (64 rows, d <= 128) for grids of at most one
  *    128-row workgroup per CU (1.5 for d <= 64; two for causal grids).
  *  - fp32: one 4-wave kernel per head dim (128 rows; 128-key tiles up to d = 64, 64-key
- *    tiles up to d = 96, 32-key tiles above), or its key split (64 rows, d <= 96) below two 128-row workgroups per CU
- *    (one per CU for non-causal d > 64, four per CU for causal grids).
+ *    tiles up to d = 96, 32-key tiles above), or its two-way key split (64 rows, d <= 96)
+ *    below two 128-row workgroups per CU (one per CU for non-causal d > 64, four per CU
+ *    for causal grids), and within that its four-way split (32 rows, 32-key tiles) for
+ *    grids of at most one 32-row workgroup per CU (four for causal grids; half a one for
+ *    d = 96).
  * The scheduling knobs of fa_fwd_config that the built-in rules set (dispatch groups of 128
  * for the causal fp32 key split, and one workgroup per CU for causal fp32 grids above d = 96
  * with at most two 128-row workgroups per CU) are not reported; they change no result bit.

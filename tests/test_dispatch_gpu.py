@@ -43,7 +43,8 @@ CASES = [
     ("bf16", 5, 8, 4352, 128, 8),  # ping-pong kernel: 17 query tiles of 256, groups of 4 pairs
     ("bf16", 5, 8, 2048, 64, 4),   # 4-wave kernel (causal, <= 4096 keys): 16 tiles, groups of 4
     ("f16", 5, 8, 2048, 36, 4),    # 4-wave kernel (d % 8 != 0): 16 tiles of 128, groups of 4
-    ("f32", 5, 8, 2048, 64, 4),    # fp32 kernel: 16 tiles of 128, groups of 4
+    ("f32", 5, 8, 2048, 64, 4),    # fp32 two-way key split: 32 tiles of 64 (dispatch groups of 128)
+    ("f32", 5, 8, 256, 64, 4),     # fp32 four-way key split: 8 tiles of 32, one group of 5 pairs
 ]
 
 

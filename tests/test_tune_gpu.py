@@ -23,7 +23,7 @@ TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
 TOL_L = 1e-3
 ALL = [{"Br": 256, "Bc": 64, "waves": 8}, {"Br": 256, "Bc": 128, "waves": 8}, {"Br": 128, "Bc": 64, "waves": 4},
        {"Br": 64, "Bc": 64, "waves": 4}, {"Br": 128, "Bc": 32, "waves": 4},
-       {"Br": 128, "Bc": 128, "waves": 4}, {"Br": 64, "Bc": 128, "waves": 4}]
+       {"Br": 128, "Bc": 128, "waves": 4}, {"Br": 64, "Bc": 128, "waves": 4}, {"Br": 32, "Bc": 32, "waves": 4}]
 
 
 def say(*a):
@@ -46,7 +46,7 @@ def admitted(dt, d, causal):
     dpad = (d + 31) // 32 * 32
     if dt == "f32":
         bc = 32 if dpad > 96 else 64
-        split = [] if dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}]
+        split = [] if dpad > 96 else [{"Br": 64, "Bc": bc, "waves": 4}, {"Br": 32, "Bc": 32, "waves": 4}]
         # 128-key tiles for 128-row workgroups up to d = 64 (16-byte rows: d % 4 == 0)
         bc128 = 128 if dpad <= 64 and d % 4 == 0 else bc
         return [{"Br": 128, "Bc": bc128, "waves": 4}] + split
