@@ -73,6 +73,7 @@ CASES = [
     ("f32", 1, 2, 300, 700, 64, False), ("f32", 1, 1, 100, 300, 128, True),
     ("bf16", 1, 2, 200, 300, 256, False), ("f16", 1, 1, 150, 170, 250, True),
     ("bf16", 1, 2, 300, 700, 32, True), ("f16", 2, 2, 257, 513, 24, False), ("f32", 1, 2, 200, 300, 32, True),
+    ("f32", 1, 2, 200, 500, 96, False), ("f32", 1, 2, 150, 400, 37, True),
 ]
 
 
