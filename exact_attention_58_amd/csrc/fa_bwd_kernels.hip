@@ -139,7 +139,8 @@ struct RowFrag {
 
 // Tile of ROWS rows x DP columns (16-bit) staged by NT threads through registers into LDS in
 // the Tile16 layout; rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 8 == 0,
-// aligned).
+// aligned). Each wave moves a contiguous run of CH x 64 chunks, one 1 KB instruction after
+// another (0-2% faster than every wave taking every (NT/64)-th KB; the same bits).
 template <int DP, bool VEC, int NT = 256, int ROWS = 64>
 struct TileCopy {
     static constexpr int CPR = DP / 8;                // 16-byte chunks per row
@@ -152,7 +153,7 @@ struct TileCopy {
         if constexpr (VEC) {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * NT;
+                const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
                 const bool ok = (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) && col < d;
                 voff[c] = ok ? (unsigned)(row * d + col) * 2u : kBufferVoid;
@@ -169,7 +170,7 @@ struct TileCopy {
         } else {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * NT;
+                const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
                 if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) r[c] = load_chunk16<VEC>(base, row0 + row, col, nrows, d);
             }
@@ -178,7 +179,7 @@ struct TileCopy {
     __device__ __attribute__((always_inline)) void store(uint16_t* lds, int tid) const {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * NT;
+            const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
             const int row = chunk / CPR;
             if (ROWS * CPR % NT == 0 || chunk < ROWS * CPR) *(u32x4*)(lds + Tile16<DP>::off(row, chunk % CPR)) = r[c];
         }
@@ -715,6 +716,7 @@ void bwd_dq_kernel(BwdArgs a, int n_qtiles) {
 
 // Tile of ROWS rows x DP columns (fp32) staged through registers into LDS rows of STR floats;
 // rows >= nrows and columns >= d are zero. VEC: 16-byte rows (d % 4 == 0, aligned buffers).
+// Each wave moves a contiguous run of chunks, as in TileCopy.
 template <int ROWS, int DP, int STR, bool VEC>
 struct TileCopy32 {
     static constexpr int CPR = DP / 4;                  // 16-byte chunks per row
@@ -726,7 +728,7 @@ struct TileCopy32 {
         if constexpr (VEC) {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * 256;
+                const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 4;
                 voff[c] = col < d ? (unsigned)(row * d + col) * 4u : kBufferVoid;
             }
@@ -740,7 +742,7 @@ struct TileCopy32 {
         } else {
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * 256;
+                const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 4;
                 r[c] = load_chunk32<VEC>(base, row0 + row, col, nrows, d);
             }
@@ -749,7 +751,7 @@ struct TileCopy32 {
     __device__ __attribute__((always_inline)) void store(float* lds, int tid) const {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int chunk = tid + c * 256;
+            const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
             const int row = chunk / CPR, col = (chunk % CPR) * 4;
             *(f32x4*)(lds + row * STR + col) = r[c];
         }
