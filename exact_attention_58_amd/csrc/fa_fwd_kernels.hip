@@ -316,12 +316,14 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
 
     // step i stages tile h * n_steps + i of every half h (rows past Nk load as zeros). With
     // 16-byte rows the chunks load through buffer resources that end at row Nk (or hold
-    // nothing for a tile past the last), at per-thread offsets fixed for every tile.
+    // nothing for a tile past the last), at per-thread offsets fixed for every tile. Each
+    // wave moves a contiguous run of CH x 64 chunks (0-3% faster than every wave taking every
+    // fourth KB; the same bits).
     u32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
     unsigned voff[CH];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-        const int chunk = tid + c * 64 * NW;
+        const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
         const int row = chunk / CPR, col = (chunk % CPR) * 8;
         voff[c] = col < d ? (unsigned)(row * d + col) * 2u : kBufferVoid;
     }
@@ -341,7 +343,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
             } else {
 #pragma unroll
                 for (int c = 0; c < CH; ++c) {
-                    const int chunk = tid + c * 64 * NW;
+                    const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                     const int row = chunk / CPR, col = (chunk % CPR) * 8;
                     kreg[h][c] = load_chunk16<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
                     vreg[h][c] = load_chunk16<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
@@ -354,7 +356,7 @@ void fwd16_kernel(FwdArgs a, int n_qtiles) {
         for (int h = 0; h < SPLIT; ++h)
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
-                const int chunk = tid + c * 64 * NW;
+                const int chunk = (tid >> 6) * (CH * 64) + c * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 8;
                 *(u32x4*)(Ksb(h) + row * KST + col) = kreg[h][c];
                 *(u32x4*)(Vsb(h) + row * VST + col) = vreg[h][c];
@@ -919,14 +921,15 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     if (CAUSAL) kv_end = min(Nk, min(q0 + BR, Nq));
     const int n_tiles = (kv_end + BC - 1) / BC;
 
-    // staging of SPLIT tiles (one per key half; rows past Nk load as zeros). With 16-byte
+    // staging of SPLIT tiles (one per key part; rows past Nk load as zeros). With 16-byte
     // rows the chunks load through buffer resources that end at row Nk (or hold nothing for
-    // a tile past the last), at per-thread offsets fixed for every tile.
+    // a tile past the last), at per-thread offsets fixed for every tile; each wave moves a
+    // contiguous run of chunks.
     f32x4 kreg[SPLIT][CH], vreg[SPLIT][CH];
     unsigned voff[CH];
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
-        const int chunk = tid + cc * 64 * NW;
+        const int chunk = (tid >> 6) * (CH * 64) + cc * 64 + (tid & 63);
         const int row = chunk / CPR, col = (chunk % CPR) * 4;
         voff[cc] = col < d ? (unsigned)(row * d + col) * 4u : kBufferVoid;
     }
@@ -943,7 +946,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
         } else {
 #pragma unroll
             for (int cc = 0; cc < CH; ++cc) {
-                const int chunk = tid + cc * 64 * NW;
+                const int chunk = (tid >> 6) * (CH * 64) + cc * 64 + (tid & 63);
                 const int row = chunk / CPR, col = (chunk % CPR) * 4;
                 kreg[h][cc] = load_chunk32<VEC>(kg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
                 vreg[h][cc] = load_chunk32<VEC>(vg, j * BC + row, col, j < n_tiles ? Nk : 0, d);
@@ -953,7 +956,7 @@ void fwd32_kernel(FwdArgs a, int n_qtiles) {
     auto store_tile_h = [&](int h, int b) __attribute__((always_inline)) {
 #pragma unroll
         for (int cc = 0; cc < CH; ++cc) {
-            const int chunk = tid + cc * 64 * NW;
+            const int chunk = (tid >> 6) * (CH * 64) + cc * 64 + (tid & 63);
             const int row = chunk / CPR, col = (chunk % CPR) * 4;
             *(f32x4*)(Ks[b] + row * KST + col) = kreg[h][cc];
             *(f32x4*)(Vs[b] + row * VST + col) = vreg[h][cc];
