@@ -37,17 +37,17 @@ KERNEL_SRC = [os.path.join(ROOT, "exact_attention_58_amd", "csrc", f)
 # recorded. Filled in from the committed profiles; a source change makes it stale (null).
 TRAFFIC = {
     # profiles/fwd32_pages_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "pages_f32": {"bytes": 67562159, "kernel_sha": "6716af35c6ea0114"},
+    "pages_f32": {"bytes": 67564207, "kernel_sha": "5f7e9dbfce818502"},
     # profiles/fwd32_tiny_causal_f32.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "tiny_causal_f32": {"bytes": 881592, "kernel_sha": "6716af35c6ea0114"},
+    "tiny_causal_f32": {"bytes": 882616, "kernel_sha": "5f7e9dbfce818502"},
     # profiles/fwd16_pp_d128_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16": {"bytes": 269676598, "kernel_sha": "6716af35c6ea0114"},
+    "d128_bf16": {"bytes": 269676802, "kernel_sha": "5f7e9dbfce818502"},
     # profiles/fwd16_pp_d128_bf16_causal.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "d128_bf16_causal": {"bytes": 354617473, "kernel_sha": "6716af35c6ea0114"},
+    "d128_bf16_causal": {"bytes": 354087341, "kernel_sha": "5f7e9dbfce818502"},
     # profiles/fwd16_pp_long_causal_bf16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "long_causal_bf16": {"bytes": 78336226, "kernel_sha": "6716af35c6ea0114"},
+    "long_causal_bf16": {"bytes": 78337608, "kernel_sha": "5f7e9dbfce818502"},
     # profiles/fwd16_split_ragged_f16.txt: FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0
-    "ragged_f16": {"bytes": 37127139, "kernel_sha": "6716af35c6ea0114"},
+    "ragged_f16": {"bytes": 37128163, "kernel_sha": "5f7e9dbfce818502"},
 }
 
 
