@@ -141,13 +141,14 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
         const int64_t split_below = causal ? 4 : c.dpad > 64 ? 1 : 2;
         if (c.dpad <= 96 && wgs128 < split_below * num_cus && Nk > 2 * c.bc) c.br = 64;
         // smaller grids still: 32 rows per workgroup, the keys in four parts, up to one such
-        // workgroup per CU (four for causal grids; half a one for d = 96, where the split
-        // runs one wave per SIMD). Measured against the two-way split (fp32, us): B1 H1 N256
-        // d64 causal 12.9 -> 9.4; B1 H2 N4096 d64 155 -> 96; B1 H16 N2048 d64 causal 106 ->
-        // 92; B2 H4 N512 d96 causal 34 -> 23; past the limits it loses (B1 H16 N2048 d64 133
-        // -> 154, B1 H16 N4096 d64 causal 290 -> 326, B1 H8 N2048 d96 122 -> 148).
+        // workgroup per CU (causal grids: four, two for d = 96, where the split runs one wave
+        // per SIMD). Measured against the two-way split (fp32, us): B1 H1 N256 d64 causal
+        // 12.9 -> 9.4; B1 H2 N4096 d64 155 -> 96; B1 H16 N2048 d64 causal 106 -> 92; B2 H4
+        // N1024 d96 64 -> 41; B2 H16 N512 d96 causal 36 -> 32; past the limits it loses (B1
+        // H16 N2048 d64 133 -> 154, B1 H16 N4096 d64 causal 290 -> 326, B1 H8 N2048 d96 122 ->
+        // 148, B1 H8 N4096 d96 causal 260 -> 304).
         const int64_t wgs32 = (Nq + 31) / 32 * B * H;
-        const int64_t four_below = c.dpad > 64 ? num_cus / 2 : causal ? 4 * (int64_t)num_cus : num_cus;
+        const int64_t four_below = (causal ? (c.dpad > 64 ? 2 : 4) : 1) * (int64_t)num_cus;
         if (c.br == 64 && wgs32 <= four_below) c.br = 32;
         // Causal grids (tuned on MI355X): the split up to four workgroups per CU, in dispatch
         // groups of 128 (B1 H16 N4096 d64: 402 -> 294 us; B1 H64 N1024: 107 -> 91 us; B1 H40

@@ -302,8 +302,7 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    tiles up to d = 96, 32-key tiles above), or its two-way key split (64 rows, d <= 96)
  *    below two 128-row workgroups per CU (one per CU for non-causal d > 64, four per CU
  *    for causal grids), and within that its four-way split (32 rows, 32-key tiles) for
- *    grids of at most one 32-row workgroup per CU (four for causal grids; half a one for
- *    d = 96).
+ *    grids of at most one 32-row workgroup per CU (causal grids: four, two for d = 96).
  * The scheduling knobs of fa_fwd_config that the built-in rules set (dispatch groups of 128
  * for the causal fp32 key split, and one workgroup per CU for causal fp32 grids above d = 96
  * with at most two 128-row workgroups per CU) are not reported; they change no result bit.

@@ -290,8 +290,7 @@ def test_select_config_fp32_key_split():
     small128 = fa.fa_select_config("f32", 1, 8, 1024, 1024, 128, False, num_cus=256)
     assert (small128["Br"], small128["Bc"]) == (128, 32)  # no split above d = 96
     assert fa.fa_select_config("f32", 4, 4, 4096, 4096, 64, False, num_cus=256)["Br"] == 128
-    # four-way split: at most one 32-row workgroup per CU (four for causal grids, half a one
-    # for d = 96)
+    # four-way split: at most one 32-row workgroup per CU (causal grids: four, two for d = 96)
     tiny = fa.fa_select_config("f32", 1, 1, 256, 256, 64, True, num_cus=256)
     assert (tiny["Br"], tiny["Bc"], tiny["waves"]) == (32, 32, 4)
     assert fa.fa_select_config("f32", 1, 8, 1024, 1024, 64, False, num_cus=256)["Br"] == 32
@@ -301,7 +300,9 @@ def test_select_config_fp32_key_split():
     assert fa.fa_select_config("f32", 1, 16, 2048, 2048, 64, True, num_cus=256)["Br"] == 32
     assert fa.fa_select_config("f32", 1, 16, 2048, 2048, 32, False, num_cus=256)["Br"] == 64
     assert fa.fa_select_config("f32", 2, 4, 512, 512, 96, True, num_cus=256)["Br"] == 32
-    assert fa.fa_select_config("f32", 2, 8, 512, 512, 96, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 2, 16, 512, 512, 96, True, num_cus=256)["Br"] == 32
+    assert fa.fa_select_config("f32", 1, 16, 2048, 2048, 96, True, num_cus=256)["Br"] == 64
+    assert fa.fa_select_config("f32", 2, 4, 1024, 1024, 96, False, num_cus=256)["Br"] == 32
     assert fa.fa_select_config("f32", 1, 8, 2048, 2048, 64, True, num_cus=64)["Br"] == 64
     assert fa.fa_select_config("f32", 1, 1, 256, 128, 64, True, num_cus=256)["Br"] == 128  # too few keys
     # up to two 128-row workgroups per CU (fp32, causal or not)
