@@ -218,6 +218,10 @@ int select_config(int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64
             // 116-119 us; B1 H56 N1024 d128, 1.75 per CU: 45.4 vs 59.9 us).
             c.br = 64;
         }
+        // causal 4-wave grids up to d = 32 in dispatch groups of 128 workgroups (three rounds
+        // each, us: B8 H16 N1536 48-54 -> 42-46; B4 H16 N4096 124-141 -> 122-136; the others
+        // measured within noise)
+        if (causal && c.waves == 4 && c.br == 128 && c.dpad <= 32) c.group = 128;
     }
     // The grid must stay within the 32-bit launch limit.
     const int64_t n_qtiles = (Nq + c.br - 1) / c.br;

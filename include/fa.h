@@ -304,8 +304,9 @@ fa_status fa_select_config(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int
  *    for causal grids), and within that its four-way split (32 rows, 32-key tiles) for
  *    grids of at most one 32-row workgroup per CU (causal grids: four, two for d = 96).
  * The scheduling knobs of fa_fwd_config that the built-in rules set (dispatch groups of 128
- * for the causal fp32 key split, and one workgroup per CU for causal fp32 grids above d = 96
- * with at most two 128-row workgroups per CU) are not reported; they change no result bit.
+ * for the causal fp32 two-way key split and for causal 16-bit 4-wave grids up to d = 32, and
+ * one workgroup per CU for causal fp32 grids above d = 96 with at most two 128-row
+ * workgroups per CU) are not reported; they change no result bit.
  */
 fa_status fa_select_config_cus(fa_dtype dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                                int64_t d, int causal, int num_cus,
